@@ -1,0 +1,63 @@
+"""The whole hot path on the CPU, step by step, in the order the pages give.
+
+Oracle code: used only by tests, smoke() and the bench's CPU baseline.
+
+forward(): bf16 Q/K/V -> (dynamic: amax of each tensor, pushed into the ring;
+static: the file values) -> descale per tensor -> e4m3 codes -> attention over
+the dequantized values, per segment, in fp64 ("Q/K/V are quantized to FP8 right
+before the attention call", vLLM page "FP8 ViT Encoder Attention", intro).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+from . import quant, scales, attention
+
+
+@dataclass
+class ForwardResult:
+    codes: tuple            # (q8, k8, v8) uint8 [T, H, d]
+    descales: np.ndarray    # fp32 [3]
+    amax: Optional[np.ndarray]  # fp32 [3] (dynamic only)
+    out: Optional[np.ndarray]   # fp64 [T, H, d] (None when attend=False)
+
+
+def quantize_step(q, k, v, mode: str, ring: Optional[scales.AmaxRing] = None, static_values=None):
+    """Scale bookkeeping + quantization for one forward."""
+    if mode == "dynamic":
+        a = np.array([quant.amax(q), quant.amax(k), quant.amax(v)], dtype=np.float32)
+        ds = scales.dynamic_descales(ring, a)
+    elif mode == "static":
+        a = None
+        ds = scales.static_descales(static_values)
+    else:
+        raise ValueError(mode)
+    codes = tuple(quant.quantize(x, d) for x, d in zip((q, k, v), ds))
+    return codes, ds, a
+
+
+def forward(q, k, v, cu_seqlens, mode: str, ring: Optional[scales.AmaxRing] = None,
+            static_values=None, softmax_scale=None, attend: bool = True) -> ForwardResult:
+    codes, ds, a = quantize_step(q, k, v, mode, ring, static_values)
+    out = None
+    if attend:
+        deq = [quant.dequantize(c, d) for c, d in zip(codes, ds)]
+        out = attention.attention(deq[0], deq[1], deq[2], cu_seqlens, softmax_scale)
+    return ForwardResult(codes, ds, a, out)
+
+
+def reference_unquantized(q, k, v, cu_seqlens, softmax_scale=None) -> np.ndarray:
+    """Attention on the bf16 values themselves (no quantization), fp64."""
+    return attention.attention(quant.bf16_to_f32(q), quant.bf16_to_f32(k), quant.bf16_to_f32(v),
+                               cu_seqlens, softmax_scale)
+
+
+def calibrate(draws, margin: float = 1.5) -> np.ndarray:
+    """16 dynamic passes over the draws, then fp32(margin x window max) per tensor."""
+    ring = scales.AmaxRing()
+    for (q, k, v) in draws:
+        ring.push([quant.amax(q), quant.amax(k), quant.amax(v)])
+    return scales.calibrated_values(ring, margin)
