@@ -1,0 +1,146 @@
+// C ABI of the library: argument validation, then launches on the caller's stream.
+// Every check happens on the host before any HIP call; nothing is allocated.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+
+#include "fp8vit.h"
+#include "fp8vit_internal.h"
+
+using fp8vit::DevState;
+
+namespace {
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline fp8vit_status from_hip(hipError_t e) { return e == hipSuccess ? FP8VIT_OK : FP8VIT_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t fp8vit_state_bytes(void) { return sizeof(DevState); }
+
+fp8vit_status fp8vit_state_init(void* d_state, void* stream) {
+  if (!d_state) return FP8VIT_ERR_INVALID_ARGUMENT;
+  if (!aligned(d_state, 256)) return FP8VIT_ERR_UNSUPPORTED;
+  return from_hip(fp8vit::launch_state_init(static_cast<DevState*>(d_state), as_stream(stream)));
+}
+
+fp8vit_status fp8vit_state_set_static(void* d_state, const float values_qkv[3], void* stream) {
+  if (!d_state || !values_qkv) return FP8VIT_ERR_INVALID_ARGUMENT;
+  if (!aligned(d_state, 256)) return FP8VIT_ERR_UNSUPPORTED;
+  for (int i = 0; i < 3; ++i)
+    if (!std::isfinite(values_qkv[i]) || !(values_qkv[i] > 0.0f)) return FP8VIT_ERR_INVALID_ARGUMENT;
+  return from_hip(fp8vit::launch_state_set_static(static_cast<DevState*>(d_state), values_qkv[0], values_qkv[1],
+                                                  values_qkv[2], as_stream(stream)));
+}
+
+fp8vit_status fp8vit_scales_update(void* d_state, const float* d_amax_qkv, void* stream) {
+  if (!d_state || !d_amax_qkv) return FP8VIT_ERR_INVALID_ARGUMENT;
+  if (!aligned(d_state, 256) || !aligned(d_amax_qkv, 4)) return FP8VIT_ERR_UNSUPPORTED;
+  return from_hip(fp8vit::launch_scales_update(static_cast<DevState*>(d_state), d_amax_qkv, as_stream(stream)));
+}
+
+fp8vit_status fp8vit_quantize_qkv(const void* q, const void* k, const void* v, int64_t ld_q, int64_t ld_k,
+                                  int64_t ld_v, int32_t total_tokens, int32_t num_heads, int32_t head_dim,
+                                  int32_t mode, void* q8, void* k8, void* v8, void* d_state, void* stream) {
+  if (!d_state || total_tokens < 0 || num_heads <= 0 || head_dim <= 0) return FP8VIT_ERR_INVALID_ARGUMENT;
+  // Empty tensors may come with null data pointers; the kernel then reads nothing.
+  if (total_tokens > 0 && (!q || !k || !v || !q8 || !k8 || !v8)) return FP8VIT_ERR_INVALID_ARGUMENT;
+  if (mode != FP8VIT_DYNAMIC && mode != FP8VIT_STATIC) return FP8VIT_ERR_INVALID_ARGUMENT;
+  const int64_t row = (int64_t)num_heads * head_dim;
+  if (ld_q < row || ld_k < row || ld_v < row) return FP8VIT_ERR_INVALID_ARGUMENT;
+  if (row % 8 != 0 || ld_q % 8 || ld_k % 8 || ld_v % 8) return FP8VIT_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(q8, 16) || !aligned(k8, 16) ||
+      !aligned(v8, 16) || !aligned(d_state, 256))
+    return FP8VIT_ERR_UNSUPPORTED;
+  // Chunk indices are 32-bit on the device.
+  if ((int64_t)total_tokens * (row / 8) >= ((int64_t)1 << 31)) return FP8VIT_ERR_UNSUPPORTED;
+  fp8vit::QuantArgs a;
+  a.x[0] = static_cast<const uint16_t*>(q);
+  a.x[1] = static_cast<const uint16_t*>(k);
+  a.x[2] = static_cast<const uint16_t*>(v);
+  a.ld[0] = ld_q;
+  a.ld[1] = ld_k;
+  a.ld[2] = ld_v;
+  a.y[0] = static_cast<uint8_t*>(q8);
+  a.y[1] = static_cast<uint8_t*>(k8);
+  a.y[2] = static_cast<uint8_t*>(v8);
+  a.T = total_tokens;
+  a.row8 = (int32_t)(row / 8);
+  a.st = static_cast<DevState*>(d_state);
+  return from_hip(fp8vit::launch_quantize(a, mode == FP8VIT_DYNAMIC, as_stream(stream)));
+}
+
+fp8vit_status fp8vit_attn_varlen(const void* q8, const void* k8, const void* v8, const int32_t* d_cu_seqlens,
+                                 int32_t num_segments, int32_t max_seqlen, int32_t total_tokens, int32_t num_heads,
+                                 int32_t head_dim, float softmax_scale, const void* d_state, void* out,
+                                 int64_t ld_out, void* stream) {
+  if (!d_cu_seqlens || !d_state) return FP8VIT_ERR_INVALID_ARGUMENT;
+  if (num_segments < 0 || max_seqlen < 0 || total_tokens < 0 || num_heads <= 0) return FP8VIT_ERR_INVALID_ARGUMENT;
+  // Empty tensors may come with null data pointers.
+  if (total_tokens > 0 && (!q8 || !k8 || !v8 || !out)) return FP8VIT_ERR_INVALID_ARGUMENT;
+  if (head_dim != 72 && head_dim != 128) return FP8VIT_ERR_UNSUPPORTED;
+  if (!std::isfinite(softmax_scale)) return FP8VIT_ERR_INVALID_ARGUMENT;
+  const int64_t row = (int64_t)num_heads * head_dim;
+  if (ld_out < row) return FP8VIT_ERR_INVALID_ARGUMENT;
+  if (ld_out % 4) return FP8VIT_ERR_UNSUPPORTED;
+  if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(out, 8) || !aligned(d_cu_seqlens, 4) ||
+      !aligned(d_state, 256))
+    return FP8VIT_ERR_UNSUPPORTED;
+  if (num_segments == 0 || total_tokens == 0 || max_seqlen == 0) return FP8VIT_OK;  // no rows to write
+  const int bm = fp8vit::attn_block_m();
+  const int64_t by_total = ((int64_t)total_tokens + bm - 1) / bm + num_segments;
+  const int64_t by_max = (int64_t)num_segments * (((int64_t)max_seqlen + bm - 1) / bm);
+  const int64_t ntiles = by_total < by_max ? by_total : by_max;
+  if (ntiles * num_heads >= ((int64_t)1 << 31)) return FP8VIT_ERR_UNSUPPORTED;
+  fp8vit::AttnArgs a;
+  a.q8 = static_cast<const uint8_t*>(q8);
+  a.k8 = static_cast<const uint8_t*>(k8);
+  a.v8 = static_cast<const uint8_t*>(v8);
+  a.cu = d_cu_seqlens;
+  a.nseg = num_segments;
+  a.H = num_heads;
+  a.ntiles_ub = (int32_t)ntiles;
+  a.st = static_cast<const DevState*>(d_state);
+  a.out = static_cast<uint16_t*>(out);
+  a.ld_out = ld_out;
+  a.softmax_scale = softmax_scale > 0.0f ? softmax_scale : (float)(1.0 / std::sqrt((double)head_dim));
+  return from_hip(fp8vit::launch_attn(a, head_dim, total_tokens, as_stream(stream)));
+}
+
+fp8vit_status fp8vit_state_read(const void* d_state, fp8vit_state_view* out, void* stream) {
+  if (!d_state || !out) return FP8VIT_ERR_INVALID_ARGUMENT;
+  if (!aligned(d_state, 256)) return FP8VIT_ERR_UNSUPPORTED;
+  DevState h;
+  hipError_t e = hipMemcpyAsync(&h, d_state, sizeof(DevState), hipMemcpyDeviceToHost, as_stream(stream));
+  if (e != hipSuccess) return FP8VIT_ERR_HIP;
+  e = hipStreamSynchronize(as_stream(stream));
+  if (e != hipSuccess) return FP8VIT_ERR_HIP;
+  std::memcpy(out->ring, h.ring, sizeof(out->ring));
+  out->count = h.count;
+  for (int i = 0; i < 3; ++i) {
+    out->static_values[i] = h.static_values[i];
+    out->descale_used[i] = h.descale_used[i];
+    out->amax_last[i] = h.amax_last[i];
+  }
+  out->flags = h.flags;
+  return FP8VIT_OK;
+}
+
+const char* fp8vit_status_str(fp8vit_status status) {
+  switch (status) {
+    case FP8VIT_OK: return "ok";
+    case FP8VIT_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case FP8VIT_ERR_UNSUPPORTED: return "unsupported (head_dim, alignment or size)";
+    case FP8VIT_ERR_HIP: return "HIP runtime error";
+    case FP8VIT_ERR_IO: return "file could not be read";
+    case FP8VIT_ERR_PARSE: return "malformed scale file";
+    case FP8VIT_ERR_NOT_FOUND: return "layer or key not found";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"
