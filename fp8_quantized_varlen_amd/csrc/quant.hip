@@ -22,9 +22,12 @@
 
 namespace fp8vit {
 
-constexpr int kQuantThreads = 256;
-constexpr int kUnroll = 4;
-constexpr uint32_t kSpinLimit = 1u << 24;
+constexpr int kQuantThreads = 512;
+constexpr int kUnroll = 8;
+// Upper bound on one grid-barrier wait, in ticks of the 100 MHz real-time
+// counter (20 ms). Reaching it means the co-residency assumption failed; the
+// state flag records it and the kernel still runs to completion.
+constexpr uint64_t kBarrierTimeoutTicks = 2000000ull;
 
 __device__ __forceinline__ uint32_t bf16_lo(uint32_t w) { return w << 16; }
 __device__ __forceinline__ uint32_t bf16_hi(uint32_t w) { return w & 0xffff0000u; }
@@ -125,14 +128,15 @@ __device__ void grid_barrier(DevState* st, uint32_t nblocks) {
       __hip_atomic_store(&st->bar_arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_fetch_add(&st->bar_generation, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     } else {
-      uint32_t spins = 0;
-      while (__hip_atomic_load(&st->bar_generation, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == gen) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++spins > kSpinLimit) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (__hip_atomic_load(&st->bar_generation, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
+        __builtin_amdgcn_s_sleep(8);
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kBarrierTimeoutTicks) {
           __hip_atomic_fetch_or(&st->flags, kFlagBarrierTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
       }
+      __atomic_thread_fence(__ATOMIC_ACQUIRE);
     }
   }
   __syncthreads();
@@ -241,7 +245,7 @@ hipError_t launch_quantize(const QuantArgs& a, bool dynamic, hipStream_t s) {
   const uint64_t want = (n8 + (uint64_t)kQuantThreads * kUnroll - 1) / ((uint64_t)kQuantThreads * kUnroll);
   if (!dynamic) {
     uint64_t g = want < 1 ? 1 : want;
-    const uint64_t cap = (uint64_t)di.cus * 8;
+    const uint64_t cap = (uint64_t)di.cus * 4;
     if (g > cap) g = cap;
     if (contig)
       hipLaunchKernelGGL(quant_static_kernel<true>, dim3((unsigned)g), dim3(kQuantThreads), 0, s, a);
@@ -249,8 +253,13 @@ hipError_t launch_quantize(const QuantArgs& a, bool dynamic, hipStream_t s) {
       hipLaunchKernelGGL(quant_static_kernel<false>, dim3((unsigned)g), dim3(kQuantThreads), 0, s, a);
     return hipGetLastError();
   }
+  // One block per CU: a small fraction of what could be resident, so all
+  // blocks are on the chip together while they wait at the grid barrier (the
+  // cooperative launch also refuses grids that could not be).
   uint64_t g = want < 1 ? 1 : want;
-  const uint64_t cap = (uint64_t)(contig ? di.coop_blocks_contig : di.coop_blocks_strided);
+  uint64_t cap = (uint64_t)di.cus;
+  const uint64_t resident = (uint64_t)(contig ? di.coop_blocks_contig : di.coop_blocks_strided);
+  if (cap > resident) cap = resident;
   if (g > cap) g = cap;
   QuantArgs args = a;
   void* params[] = {&args};
