@@ -9,22 +9,28 @@
 // Design (MI355X-first, not a port of any kernel on the pages):
 //  * One workgroup = 4 waves = 128 queries of one (segment, head); each wave
 //    owns 32 queries (two 16-query MFMA column blocks).
-//  * K/V tiles of 128 keys are staged in LDS. S^T = K Q^T is computed with
-//    v_mfma_f32_16x16x128_f8f6f4 (K rows as the A operand, Q as B), d padded to
-//    128 with zeros for head_dim 72. The A rows are permuted so that lane group
-//    g ends up holding keys 32g..32g+31 of its query: the fp32 S^T registers
-//    convert in place into the B operand of the next product, no LDS round trip.
-//  * O^T = V^T P^T on the same MFMA: V^T comes from row-major V in LDS through
+//  * K/V tiles of 128 keys are double-buffered in LDS. The next tile's global
+//    loads are issued into registers before the current tile is computed and
+//    written to the other LDS buffer after it: one barrier per tile, global
+//    latency hidden behind the MFMA/softmax work.
+//  * S^T = K Q^T on v_mfma_f32_16x16x128_f8f6f4 (K rows as the A operand, Q as
+//    B), d zero-padded to 128 for head_dim 72. A rows are permuted so that lane
+//    group g holds keys 32g..32g+31 of its query: the fp32 S^T registers turn
+//    in place into the B operand of the next product (no LDS round trip).
+//  * O^T = V^T P^T on the same MFMA; V^T comes from row-major V in LDS through
 //    ds_read_b64_tr_b8 (byte transpose on read). Column 72 of the hd72 V tile
 //    holds 1.0, so the same MFMAs accumulate the row sum of the probabilities
 //    actually used; hd128 appends a constant ones block.
-//  * Online softmax in exp2 units with a lazy reference max: O is rescaled only
-//    when a row max grows by more than 1.75, and P~ = 2^7 * exp2(t - m_ref) stays
-//    below 2^8.75 < 448, inside e4m3's range.
-//  * P~ goes to the FP8 MFMA in two e4m3 terms, hi = e4m3(P~) and
+//  * One-pass online softmax in exp2 units with a lazy reference max m_ref:
+//    P~ = 2^7 * exp2(t - m_ref) is formed right after each 16-key S^T block
+//    while a per-lane running max is kept. Only if some score of the tile
+//    exceeds m_ref + 1.75 (then P~ could pass 448, e4m3's largest value) is
+//    the row max reduced across lanes, O rescaled, and the tile's S^T/P~
+//    recomputed. The first tile always takes that path (m_ref = -inf).
+//  * P~ goes to the FP8 MFMA as two e4m3 terms, hi = e4m3(P~) and
 //    lo = e4m3(P~ - hi): a single e4m3 term adds ~2.5% relative error to O.
 //  * Work items are (head, query tile); consecutive items of one head are
-//    mapped to the same XCD so K/V re-reads hit that XCD's L2.
+//    mapped to the same XCD so that K/V re-reads hit that XCD's L2.
 #include "fp8vit_internal.h"
 
 namespace fp8vit {
@@ -32,6 +38,8 @@ namespace fp8vit {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 
 constexpr int kWaves = 4;
@@ -46,13 +54,20 @@ constexpr float kLog2e = 1.4426950408889634f;
 template <int D> struct Cfg;
 // KS/VS: LDS row strides (bytes) chosen so 16 lanes reading 16 B from 16 rows,
 // or 8 rows x 16 B for the transpose read, touch distinct banks.
-// NCB: 16-column blocks of O^T including the ones column. CH x CHB: global
-// chunks per K/V row.
+// NCB: 16-column blocks of O^T including the ones column.
+// CHB: bytes per global load; NLD: loads per thread per tensor and tile.
 template <> struct Cfg<72> {
-  static constexpr int KS = 112, VS = 80, NCB = 5, CH = 9, CHB = 8, ONES_CB = 4, ONES_LANE0 = 32;
+  static constexpr int KS = 112, VS = 80, NCB = 5, CHB = 8, ROWCH = 9, ONES_CB = 4, ONES_LANE0 = 32;
 };
 template <> struct Cfg<128> {
-  static constexpr int KS = 144, VS = 144, NCB = 9, CH = 8, CHB = 16, ONES_CB = 8, ONES_LANE0 = 0;
+  static constexpr int KS = 144, VS = 144, NCB = 9, CHB = 16, ROWCH = 8, ONES_CB = 8, ONES_LANE0 = 0;
+};
+
+template <int D> struct Stage {
+  static constexpr int NCHUNK = kBN * Cfg<D>::ROWCH;                    // chunks per tensor and tile
+  static constexpr int NLD = (NCHUNK + kThreads - 1) / kThreads;        // per thread
+  static constexpr int KBUF = kBN * Cfg<D>::KS, VBUF = kBN * Cfg<D>::VS;
+  using chunk_t = typename std::conditional<Cfg<D>::CHB == 8, u32x2, u32x4>::type;
 };
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
@@ -64,11 +79,90 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Global -> register prefetch of one K/V tile (rows past the segment end read
+// the last valid row: those keys are masked or multiplied by P = 0).
 template <int D>
-__global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
+__device__ __forceinline__ void prefetch_tile(const AttnArgs& a, int s0, int L, int h, int kv0, int tid,
+                                              typename Stage<D>::chunk_t* kr, typename Stage<D>::chunk_t* vr) {
+  using S = Stage<D>;
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kBN * C::KS];
-  __shared__ __attribute__((aligned(16))) uint8_t v_lds[kBN * C::VS];
+#pragma unroll
+  for (int i = 0; i < S::NLD; ++i) {
+    const int c = tid + i * kThreads;
+    if (S::NCHUNK % kThreads == 0 || c < S::NCHUNK) {
+      const int row = c / C::ROWCH, part = c - row * C::ROWCH;
+      const int key = min(kv0 + row, L - 1);
+      const int64_t off = ((int64_t)(s0 + key) * a.H + h) * D + C::CHB * part;
+      kr[i] = *reinterpret_cast<const typename S::chunk_t*>(a.k8 + off);
+      vr[i] = *reinterpret_cast<const typename S::chunk_t*>(a.v8 + off);
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void commit_tile(uint8_t* kb, uint8_t* vb, int tid, const typename Stage<D>::chunk_t* kr,
+                                            const typename Stage<D>::chunk_t* vr) {
+  using S = Stage<D>;
+  using C = Cfg<D>;
+#pragma unroll
+  for (int i = 0; i < S::NLD; ++i) {
+    const int c = tid + i * kThreads;
+    if (S::NCHUNK % kThreads == 0 || c < S::NCHUNK) {
+      const int row = c / C::ROWCH, part = c - row * C::ROWCH;
+      *reinterpret_cast<typename S::chunk_t*>(kb + row * C::KS + C::CHB * part) = kr[i];
+      *reinterpret_cast<typename S::chunk_t*>(vb + row * C::VS + C::CHB * part) = vr[i];
+    }
+  }
+}
+
+// A operand of S^T block t: lane row i16 <-> key 32*(i16/4) + 4t + i16%4, d bytes 32g..32g+31.
+template <int D>
+__device__ __forceinline__ v8i k_operand(const uint8_t* kb, int t, int g, int i16) {
+  const int krow = 32 * (i16 >> 2) + 4 * t + (i16 & 3);
+  const int koff = (D == 72 && g == 3) ? 80 : 32 * g;     // hd72: bytes 72..111 of a row are zero
+  const uint8_t* kp = kb + krow * Cfg<D>::KS + koff;
+  const uint4 k0 = *reinterpret_cast<const uint4*>(kp);
+  const uint4 k1 = *reinterpret_cast<const uint4*>(kp + 16);
+  return v8i{(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w, (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
+}
+
+// A operand of O^T block cb: lane row i16 <-> V column 16cb + i16, keys 32g..32g+31,
+// gathered from row-major V by the byte-transposing LDS read.
+template <int D>
+__device__ __forceinline__ v8i v_operand(const uint8_t* vb, int cb, int g, int i16) {
+  v8i r;
+#pragma unroll
+  for (int sidx = 0; sidx < 4; ++sidx) {
+    const uint8_t* vp = vb + (32 * g + 8 * sidx + (i16 >> 1)) * Cfg<D>::VS + 16 * cb + 8 * (i16 & 1);
+    const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vp));
+    r[2 * sidx] = x[0];
+    r[2 * sidx + 1] = x[1];
+  }
+  return r;
+}
+
+// Two e4m3 terms of four probabilities P~ = exp2(s*c + nb), packed as one
+// dword of the P^T operand (hi) and one of the correction term (lo).
+__device__ __forceinline__ int2 probs_to_fp8(const v4f& s, float c, float nb) {
+  const float p0 = __builtin_amdgcn_exp2f(fmaf(s[0], c, nb));
+  const float p1 = __builtin_amdgcn_exp2f(fmaf(s[1], c, nb));
+  const float p2 = __builtin_amdgcn_exp2f(fmaf(s[2], c, nb));
+  const float p3 = __builtin_amdgcn_exp2f(fmaf(s[3], c, nb));
+  int h = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+  h = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, h, true);
+  const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
+  const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
+  int l = __builtin_amdgcn_cvt_pk_fp8_f32(p0 - h01[0], p1 - h01[1], 0, false);
+  l = __builtin_amdgcn_cvt_pk_fp8_f32(p2 - h23[0], p3 - h23[1], l, true);
+  return make_int2(h, l);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 72 ? 2 : 1, 2))) void attn_kernel(AttnArgs a) {
+  using C = Cfg<D>;
+  using S = Stage<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[2 * S::KBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds[2 * S::VBUF];
 
   // ---- work item: XCD-grouped (head, query tile) -> segment by prefix scan ----
   const int G = gridDim.x;
@@ -85,13 +179,16 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   }
   if (L <= 0) return;
   const int q0 = tile * kBM;
+  const int ntiles = (L + kBN - 1) / kBN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, i16 = lane & 15;
 
-  // ---- constant parts of the LDS tiles: zero padding, ones column ----
-  for (int r = tid; r < kBN; r += kThreads) {
+  // ---- first K/V tile in flight while the constant parts are written ----
+  typename S::chunk_t kr[S::NLD], vr[S::NLD];
+  prefetch_tile<D>(a, s0, L, h, 0, tid, kr, vr);
+  for (int r = tid; r < 2 * kBN; r += kThreads) {
 #pragma unroll
     for (int b = D; b < C::KS; b += 8) *reinterpret_cast<uint2*>(k_lds + r * C::KS + b) = make_uint2(0u, 0u);
 #pragma unroll
@@ -100,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   }
 
   const float dq = a.st->descale_used[0], dk = a.st->descale_used[1], dv = a.st->descale_used[2];
-  const float cexp = a.softmax_scale * dq * dk * kLog2e;   // raw score -> log2 units
+  const float cexp = a.softmax_scale * dq * dk * kLog2e;   // raw score -> log2 units (> 0)
 
   // ---- Q operands (B of S^T): lane holds query i16 of its block, d bytes 32g.. ----
   v8i qop[2];
@@ -136,137 +233,88 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
     for (int cb = 0; cb < C::NCB; ++cb) o[qb][cb] = v4f{0.f, 0.f, 0.f, 0.f};
-  float mref[2] = {-INFINITY, -INFINITY};
-  const v8i ones_op = (i16 == 0) ? v8i{0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                                       0x38383838, 0x38383838}
-                                 : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  float mref[2] = {-INFINITY, -INFINITY};   // reference max, log2 units
+  float thr[2] = {-INFINITY, -INFINITY};    // raw-score threshold (m_ref + lazy) / c
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
 
-  for (int kv0 = 0; kv0 < L; kv0 += kBN) {
-    // ---- stage K and V rows kv0..kv0+127 (zeros past the segment end) ----
-    __syncthreads();
-    for (int c = tid; c < kBN * C::CH; c += kThreads) {
-      const int row = c / C::CH, part = c - row * C::CH;
-      const int key = kv0 + row;
-      if (C::CHB == 8) {
-        uint2 kk = make_uint2(0u, 0u), vv = make_uint2(0u, 0u);
-        if (key < L) {
-          const int64_t off = ((int64_t)(s0 + key) * a.H + h) * D + 8 * part;
-          kk = *reinterpret_cast<const uint2*>(a.k8 + off);
-          vv = *reinterpret_cast<const uint2*>(a.v8 + off);
-        }
-        *reinterpret_cast<uint2*>(k_lds + row * C::KS + 8 * part) = kk;
-        *reinterpret_cast<uint2*>(v_lds + row * C::VS + 8 * part) = vv;
-      } else {
-        uint4 kk = make_uint4(0u, 0u, 0u, 0u), vv = make_uint4(0u, 0u, 0u, 0u);
-        if (key < L) {
-          const int64_t off = ((int64_t)(s0 + key) * a.H + h) * D + 16 * part;
-          kk = *reinterpret_cast<const uint4*>(a.k8 + off);
-          vv = *reinterpret_cast<const uint4*>(a.v8 + off);
-        }
-        *reinterpret_cast<uint4*>(k_lds + row * C::KS + 16 * part) = kk;
-        *reinterpret_cast<uint4*>(v_lds + row * C::VS + 16 * part) = vv;
-      }
-    }
-    __syncthreads();
+  commit_tile<D>(k_lds, v_lds, tid, kr, vr);
+  __syncthreads();
 
-    // ---- S^T = K Q^T: 8 key tiles x 2 query blocks ----
-    float s[2][8][4];
+  for (int j = 0; j < ntiles; ++j) {
+    const int kv0 = j * kBN;
+    const uint8_t* kb = k_lds + (j & 1) * S::KBUF;
+    const uint8_t* vb = v_lds + (j & 1) * S::VBUF;
+    if (j + 1 < ntiles) prefetch_tile<D>(a, s0, L, h, kv0 + kBN, tid, kr, vr);
+    const bool partial = kv0 + kBN > L;
+
+    // ---- S^T and P~ per 16-key block, with the running per-lane max ----
+    v8i phi[2], plo[2];
+    float lm[2] = {-INFINITY, -INFINITY};
+    auto run_pass = [&]() {
+      const float nb0 = kExpBias - mref[0], nb1 = kExpBias - mref[1];
+      v8i knext = k_operand<D>(kb, 0, g, i16);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int krow = 32 * (i16 >> 2) + 4 * t + (i16 & 3);
-      const int koff = (D == 72 && g == 3) ? 80 : 32 * g;
-      const uint8_t* kp = k_lds + krow * C::KS + koff;
-      const uint4 k0 = *reinterpret_cast<const uint4*>(kp);
-      const uint4 k1 = *reinterpret_cast<const uint4*>(kp + 16);
-      const v8i kop = {(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w, (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
+      for (int t = 0; t < 8; ++t) {
+        const v8i kop = knext;
+        if (t + 1 < 8) knext = k_operand<D>(kb, t + 1, g, i16);
+        v4f s0v = mfma_fp8(kop, qop[0], zero4);
+        v4f s1v = mfma_fp8(kop, qop[1], zero4);
+        if (partial) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool oob = kv0 + 32 * g + 4 * t + r >= L;
+            s0v[r] = oob ? -INFINITY : s0v[r];
+            s1v[r] = oob ? -INFINITY : s1v[r];
+          }
+        }
+        lm[0] = fmaxf(fmaxf(lm[0], fmaxf(s0v[0], s0v[1])), fmaxf(s0v[2], s0v[3]));
+        lm[1] = fmaxf(fmaxf(lm[1], fmaxf(s1v[0], s1v[1])), fmaxf(s1v[2], s1v[3]));
+        const int2 p0 = probs_to_fp8(s0v, cexp, nb0);
+        const int2 p1 = probs_to_fp8(s1v, cexp, nb1);
+        phi[0][t] = p0.x;
+        plo[0][t] = p0.y;
+        phi[1][t] = p1.x;
+        plo[1][t] = p1.y;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    run_pass();
+    // Overflow check: a score above its row's threshold means P~ may exceed
+    // 448. Then reduce the row max over the four lane groups, move the
+    // reference max, rescale O and recompute this tile's probabilities.
+    if (__ballot(lm[0] > thr[0] || lm[1] > thr[1]) != 0ull) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const v4f acc = mfma_fp8(kop, qop[qb], zero4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s[qb][t][r] = acc[r];
-      }
-    }
-    // keys of this lane: kv0 + 32g + 4t + r
-    if (kv0 + kBN > L) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (kv0 + 32 * g + 4 * t + r >= L) s[qb][t][r] = -INFINITY;
-    }
-
-    // ---- row max (4 lane groups share a query) and lazy rescale ----
-    float mt[2];
-    bool need = false;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float m = s[qb][0][0];
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) m = fmaxf(m, s[qb][t][r]);
-      m = fmaxf(m, __shfl_xor(m, 16, 64));
-      m = fmaxf(m, __shfl_xor(m, 32, 64));
-      mt[qb] = m * cexp;
-      need = need || (mt[qb] > mref[qb] + kLazy);
-    }
-    if (__ballot(need) != 0ull) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const float mn = fmaxf(mref[qb], mt[qb]);
+        float m = lm[qb];
+        m = fmaxf(m, __shfl_xor(m, 16, 64));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        const float mn = fmaxf(mref[qb], m * cexp);
         const float alpha = __builtin_amdgcn_exp2f(mref[qb] - mn);
         mref[qb] = mn;
+        thr[qb] = (mn + kLazy) / cexp;
 #pragma unroll
         for (int cb = 0; cb < C::NCB; ++cb) o[qb][cb] *= alpha;
       }
-    }
-
-    // ---- P~ in two e4m3 terms, packed straight into the B operand layout ----
-    v8i phi[2], plo[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const float nb = kExpBias - mref[qb];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[qb][t][0], cexp, nb));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[qb][t][1], cexp, nb));
-        const float p2 = __builtin_amdgcn_exp2f(fmaf(s[qb][t][2], cexp, nb));
-        const float p3 = __builtin_amdgcn_exp2f(fmaf(s[qb][t][3], cexp, nb));
-        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-        hi = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, hi, true);
-        const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
-        const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p0 - h01[0], p1 - h01[1], 0, false);
-        lo = __builtin_amdgcn_cvt_pk_fp8_f32(p2 - h23[0], p3 - h23[1], lo, true);
-        phi[qb][t] = hi;
-        plo[qb][t] = lo;
-      }
+      run_pass();
     }
 
     // ---- O^T += V^T P^T (hi and lo terms) ----
 #pragma unroll
     for (int cb = 0; cb < C::NCB; ++cb) {
-      v8i vop;
-      if (D == 128 && cb == 8) {
-        vop = ones_op;
-      } else {
-#pragma unroll
-        for (int sidx = 0; sidx < 4; ++sidx) {
-          const uint8_t* vp = v_lds + (32 * g + 8 * sidx + (i16 >> 1)) * C::VS + 16 * cb + 8 * (i16 & 1);
-          const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vp));
-          vop[2 * sidx] = r[0];
-          vop[2 * sidx + 1] = r[1];
-        }
-      }
+      const v8i vop = (D == 128 && cb == 8)
+                          ? ((i16 == 0) ? v8i{0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                                              0x38383838, 0x38383838, 0x38383838}
+                                        : v8i{0, 0, 0, 0, 0, 0, 0, 0})
+                          : v_operand<D>(vb, cb, g, i16);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         o[qb][cb] = mfma_fp8(vop, phi[qb], o[qb][cb]);
         o[qb][cb] = mfma_fp8(vop, plo[qb], o[qb][cb]);
       }
     }
+
+    if (j + 1 < ntiles) commit_tile<D>(k_lds + ((j + 1) & 1) * S::KBUF, v_lds + ((j + 1) & 1) * S::VBUF, tid, kr, vr);
+    __syncthreads();
   }
 
   // ---- epilogue: divide by the row sum (ones column), scale by dv, bf16 ----
