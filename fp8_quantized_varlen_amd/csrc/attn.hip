@@ -63,10 +63,18 @@ template <> struct Cfg<128> {
   static constexpr int KS = 144, VS = 144, NCB = 9, CHB = 16, ROWCH = 8, ONES_CB = 8, ONES_LANE0 = 0;
 };
 
+// LDS placement of a tile's rows.
+//  K: key k sits in row 4*(k%32) + k/32, so the 16 keys of one S^T block
+//     (32a + 4t + b, a, b = 0..3) occupy 16 consecutive rows 16t..16t+15.
+//  V: key k sits at byte k*VS + 64*(k/32); the 64-byte gap between 32-key
+//     groups spreads the four lane groups of a transpose read over the banks.
+__device__ __forceinline__ int k_row(int key) { return 4 * (key & 31) + (key >> 5); }
+template <int D> __device__ __forceinline__ int v_off(int key) { return key * Cfg<D>::VS + 64 * (key >> 5); }
+
 template <int D> struct Stage {
   static constexpr int NCHUNK = kBN * Cfg<D>::ROWCH;                    // chunks per tensor and tile
   static constexpr int NLD = (NCHUNK + kThreads - 1) / kThreads;        // per thread
-  static constexpr int KBUF = kBN * Cfg<D>::KS, VBUF = kBN * Cfg<D>::VS;
+  static constexpr int KBUF = kBN * Cfg<D>::KS, VBUF = kBN * Cfg<D>::VS + 64 * (kBN / 32 - 1);
   using chunk_t = typename std::conditional<Cfg<D>::CHB == 8, u32x2, u32x4>::type;
 };
 
@@ -109,21 +117,22 @@ __device__ __forceinline__ void commit_tile(uint8_t* kb, uint8_t* vb, int tid, c
     const int c = tid + i * kThreads;
     if (S::NCHUNK % kThreads == 0 || c < S::NCHUNK) {
       const int row = c / C::ROWCH, part = c - row * C::ROWCH;
-      *reinterpret_cast<typename S::chunk_t*>(kb + row * C::KS + C::CHB * part) = kr[i];
-      *reinterpret_cast<typename S::chunk_t*>(vb + row * C::VS + C::CHB * part) = vr[i];
+      *reinterpret_cast<typename S::chunk_t*>(kb + k_row(row) * C::KS + C::CHB * part) = kr[i];
+      *reinterpret_cast<typename S::chunk_t*>(vb + v_off<D>(row) + C::CHB * part) = vr[i];
     }
   }
 }
 
 // A operand of S^T block t: lane row i16 <-> key 32*(i16/4) + 4t + i16%4, d bytes 32g..32g+31.
+typedef int v4i __attribute__((ext_vector_type(4)));
 template <int D>
 __device__ __forceinline__ v8i k_operand(const uint8_t* kb, int t, int g, int i16) {
-  const int krow = 32 * (i16 >> 2) + 4 * t + (i16 & 3);
+  const int krow = 16 * t + 4 * (i16 & 3) + (i16 >> 2);   // = k_row(32*(i16/4) + 4t + i16%4)
   const int koff = (D == 72 && g == 3) ? 80 : 32 * g;     // hd72: bytes 72..111 of a row are zero
   const uint8_t* kp = kb + krow * Cfg<D>::KS + koff;
-  const uint4 k0 = *reinterpret_cast<const uint4*>(kp);
-  const uint4 k1 = *reinterpret_cast<const uint4*>(kp + 16);
-  return v8i{(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w, (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
+  const v4i k0 = *reinterpret_cast<const v4i*>(kp);
+  const v4i k1 = *reinterpret_cast<const v4i*>(kp + 16);
+  return __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // A operand of O^T block cb: lane row i16 <-> V column 16cb + i16, keys 32g..32g+31,
@@ -133,7 +142,7 @@ __device__ __forceinline__ v8i v_operand(const uint8_t* vb, int cb, int g, int i
   v8i r;
 #pragma unroll
   for (int sidx = 0; sidx < 4; ++sidx) {
-    const uint8_t* vp = vb + (32 * g + 8 * sidx + (i16 >> 1)) * Cfg<D>::VS + 16 * cb + 8 * (i16 & 1);
+    const uint8_t* vp = vb + v_off<D>(32 * g + 8 * sidx + (i16 >> 1)) + 16 * cb + 8 * (i16 & 1);
     const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vp));
     r[2 * sidx] = x[0];
     r[2 * sidx + 1] = x[1];
@@ -189,11 +198,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 7
   typename S::chunk_t kr[S::NLD], vr[S::NLD];
   prefetch_tile<D>(a, s0, L, h, 0, tid, kr, vr);
   for (int r = tid; r < 2 * kBN; r += kThreads) {
+    uint8_t* kr0 = k_lds + (r / kBN) * S::KBUF + (r % kBN) * C::KS;
+    uint8_t* vr0 = v_lds + (r / kBN) * S::VBUF + v_off<D>(r % kBN);
 #pragma unroll
-    for (int b = D; b < C::KS; b += 8) *reinterpret_cast<uint2*>(k_lds + r * C::KS + b) = make_uint2(0u, 0u);
+    for (int b = D; b < C::KS; b += 8) *reinterpret_cast<uint2*>(kr0 + b) = make_uint2(0u, 0u);
 #pragma unroll
     for (int b = D; b < C::VS; b += 8)
-      *reinterpret_cast<uint2*>(v_lds + r * C::VS + b) = make_uint2((D == 72 && b == 72) ? 0x38u : 0u, 0u);
+      *reinterpret_cast<uint2*>(vr0 + b) = make_uint2((D == 72 && b == 72) ? 0x38u : 0u, 0u);
   }
 
   const float dq = a.st->descale_used[0], dk = a.st->descale_used[1], dv = a.st->descale_used[2];
@@ -247,38 +258,54 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 7
     if (j + 1 < ntiles) prefetch_tile<D>(a, s0, L, h, kv0 + kBN, tid, kr, vr);
     const bool partial = kv0 + kBN > L;
 
+
     // ---- S^T and P~ per 16-key block, with the running per-lane max ----
     v8i phi[2], plo[2];
     float lm[2] = {-INFINITY, -INFINITY};
-    auto run_pass = [&]() {
+    // S^T of block t+1 is issued on the matrix core before the softmax VALU
+    // work of block t, so the two overlap within the wave.
+    const bool has_next = j + 1 < ntiles;
+    auto run_pass = [&](bool commit_here) {
       const float nb0 = kExpBias - mref[0], nb1 = kExpBias - mref[1];
-      v8i knext = k_operand<D>(kb, 0, g, i16);
+      v8i kop = k_operand<D>(kb, 0, g, i16);
+      v4f sa0 = mfma_fp8(kop, qop[0], zero4);
+      v4f sa1 = mfma_fp8(kop, qop[1], zero4);
+      kop = k_operand<D>(kb, 1, g, i16);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const v8i kop = knext;
-        if (t + 1 < 8) knext = k_operand<D>(kb, t + 1, g, i16);
-        v4f s0v = mfma_fp8(kop, qop[0], zero4);
-        v4f s1v = mfma_fp8(kop, qop[1], zero4);
+        v4f sb0, sb1;
+        if (t + 1 < 8) {
+          sb0 = mfma_fp8(kop, qop[0], zero4);
+          sb1 = mfma_fp8(kop, qop[1], zero4);
+          if (t + 2 < 8) kop = k_operand<D>(kb, t + 2, g, i16);
+        }
         if (partial) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const bool oob = kv0 + 32 * g + 4 * t + r >= L;
-            s0v[r] = oob ? -INFINITY : s0v[r];
-            s1v[r] = oob ? -INFINITY : s1v[r];
+            sa0[r] = oob ? -INFINITY : sa0[r];
+            sa1[r] = oob ? -INFINITY : sa1[r];
           }
         }
-        lm[0] = fmaxf(fmaxf(lm[0], fmaxf(s0v[0], s0v[1])), fmaxf(s0v[2], s0v[3]));
-        lm[1] = fmaxf(fmaxf(lm[1], fmaxf(s1v[0], s1v[1])), fmaxf(s1v[2], s1v[3]));
-        const int2 p0 = probs_to_fp8(s0v, cexp, nb0);
-        const int2 p1 = probs_to_fp8(s1v, cexp, nb1);
+        lm[0] = fmaxf(fmaxf(fmaxf(fmaxf(lm[0], sa0[0]), sa0[1]), sa0[2]), sa0[3]);
+        lm[1] = fmaxf(fmaxf(fmaxf(fmaxf(lm[1], sa1[0]), sa1[1]), sa1[2]), sa1[3]);
+        const int2 p0 = probs_to_fp8(sa0, cexp, nb0);
+        const int2 p1 = probs_to_fp8(sa1, cexp, nb1);
         phi[0][t] = p0.x;
         plo[0][t] = p0.y;
         phi[1][t] = p1.x;
         plo[1][t] = p1.y;
-        __builtin_amdgcn_sched_barrier(0);
+        if (t + 1 < 8) {
+          sa0 = sb0;
+          sa1 = sb1;
+        }
+        // The other buffer is free since the last barrier: store the next
+        // tile early so its registers do not stay live through the pass.
+        if (t == 3 && commit_here && has_next)
+          commit_tile<D>(k_lds + ((j + 1) & 1) * S::KBUF, v_lds + ((j + 1) & 1) * S::VBUF, tid, kr, vr);
       }
     };
-    run_pass();
+    run_pass(true);
     // Overflow check: a score above its row's threshold means P~ may exceed
     // 448. Then reduce the row max over the four lane groups, move the
     // reference max, rescale O and recompute this tile's probabilities.
@@ -295,7 +322,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 7
 #pragma unroll
         for (int cb = 0; cb < C::NCB; ++cb) o[qb][cb] *= alpha;
       }
-      run_pass();
+      run_pass(false);
     }
 
     // ---- O^T += V^T P^T (hi and lo terms) ----
@@ -313,7 +340,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 7
       }
     }
 
-    if (j + 1 < ntiles) commit_tile<D>(k_lds + ((j + 1) & 1) * S::KBUF, v_lds + ((j + 1) & 1) * S::VBUF, tid, kr, vr);
     __syncthreads();
   }
 
