@@ -7,12 +7,12 @@
 // with Q8/K8/V8 the e4m3 codes and dq/dk/dv the per-tensor descales.
 //
 // Design (MI355X-first, not a port of any kernel on the pages):
-//  * One workgroup = 4 waves = 128 queries of one (segment, head); each wave
-//    owns 32 queries (two 16-query MFMA column blocks).
+//  * A workgroup owns 128 queries of one (segment, head): WAVES waves of
+//    QB 16-query MFMA column blocks each (8x1 or 4x2).
 //  * K/V tiles of 128 keys are double-buffered in LDS. The next tile's global
-//    loads are issued into registers before the current tile is computed and
-//    written to the other LDS buffer after it: one barrier per tile, global
-//    latency hidden behind the MFMA/softmax work.
+//    loads are issued into registers when a tile starts and stored into the
+//    other buffer halfway through it: one barrier per tile, global latency
+//    hidden behind the MFMA/softmax work.
 //  * S^T = K Q^T on v_mfma_f32_16x16x128_f8f6f4 (K rows as the A operand, Q as
 //    B), d zero-padded to 128 for head_dim 72. A rows are permuted so that lane
 //    group g holds keys 32g..32g+31 of its query: the fp32 S^T registers turn
@@ -23,57 +23,60 @@
 //    actually used; hd128 appends a constant ones block.
 //  * One-pass online softmax in exp2 units with a lazy reference max m_ref:
 //    P~ = 2^7 * exp2(t - m_ref) is formed right after each 16-key S^T block
-//    while a per-lane running max is kept. Only if some score of the tile
-//    exceeds m_ref + 1.75 (then P~ could pass 448, e4m3's largest value) is
-//    the row max reduced across lanes, O rescaled, and the tile's S^T/P~
-//    recomputed. The first tile always takes that path (m_ref = -inf).
+//    while a per-lane running max is kept; S^T of the next block is already on
+//    the matrix core. Only if some score of the tile exceeds m_ref + 1.75
+//    (then P~ could pass 448, e4m3's largest value) is the row max reduced
+//    across lanes, O rescaled and the tile's probabilities recomputed. The
+//    first tile always takes that path (m_ref = -inf).
 //  * P~ goes to the FP8 MFMA as two e4m3 terms, hi = e4m3(P~) and
 //    lo = e4m3(P~ - hi): a single e4m3 term adds ~2.5% relative error to O.
 //  * Work items are (head, query tile); consecutive items of one head are
 //    mapped to the same XCD so that K/V re-reads hit that XCD's L2.
+#include <type_traits>
+
 #include "fp8vit_internal.h"
 
 namespace fp8vit {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBMW = 32;             // queries per wave
-constexpr int kBM = kWaves * kBMW;   // queries per workgroup
+constexpr int kBM = 128;             // queries per workgroup
 constexpr int kBN = 128;             // keys per tile
 constexpr float kExpBias = 7.0f;     // P~ = 2^7 * exp2(t - m_ref)
 constexpr float kLazy = 1.75f;       // log2 growth of the max tolerated before rescaling
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D> struct Cfg;
-// KS/VS: LDS row strides (bytes) chosen so 16 lanes reading 16 B from 16 rows,
-// or 8 rows x 16 B for the transpose read, touch distinct banks.
-// NCB: 16-column blocks of O^T including the ones column.
-// CHB: bytes per global load; NLD: loads per thread per tensor and tile.
+// KS/VS: LDS row strides in bytes. NCB: 16-column blocks of O^T including the
+// ones column. CHB x ROWCH: bytes per global load x loads per K/V row.
 template <> struct Cfg<72> {
   static constexpr int KS = 112, VS = 80, NCB = 5, CHB = 8, ROWCH = 9, ONES_CB = 4, ONES_LANE0 = 32;
+  static constexpr int WAVES = 8, QB = 1, MIN_WAVES_PER_EU = 4;
 };
 template <> struct Cfg<128> {
   static constexpr int KS = 144, VS = 144, NCB = 9, CHB = 16, ROWCH = 8, ONES_CB = 8, ONES_LANE0 = 0;
+  static constexpr int WAVES = 8, QB = 1, MIN_WAVES_PER_EU = 2;
 };
 
 // LDS placement of a tile's rows.
 //  K: key k sits in row 4*(k%32) + k/32, so the 16 keys of one S^T block
-//     (32a + 4t + b, a, b = 0..3) occupy 16 consecutive rows 16t..16t+15.
+//     (32a + 4t + b, a, b = 0..3) occupy 16 consecutive rows 16t..16t+15,
+//     whose 16-byte pieces fall on distinct banks.
 //  V: key k sits at byte k*VS + 64*(k/32); the 64-byte gap between 32-key
 //     groups spreads the four lane groups of a transpose read over the banks.
 __device__ __forceinline__ int k_row(int key) { return 4 * (key & 31) + (key >> 5); }
 template <int D> __device__ __forceinline__ int v_off(int key) { return key * Cfg<D>::VS + 64 * (key >> 5); }
 
 template <int D> struct Stage {
+  static constexpr int THREADS = 64 * Cfg<D>::WAVES;
   static constexpr int NCHUNK = kBN * Cfg<D>::ROWCH;                    // chunks per tensor and tile
-  static constexpr int NLD = (NCHUNK + kThreads - 1) / kThreads;        // per thread
+  static constexpr int NLD = (NCHUNK + THREADS - 1) / THREADS;          // per thread
   static constexpr int KBUF = kBN * Cfg<D>::KS, VBUF = kBN * Cfg<D>::VS + 64 * (kBN / 32 - 1);
   using chunk_t = typename std::conditional<Cfg<D>::CHB == 8, u32x2, u32x4>::type;
 };
@@ -96,8 +99,8 @@ __device__ __forceinline__ void prefetch_tile(const AttnArgs& a, int s0, int L, 
   using C = Cfg<D>;
 #pragma unroll
   for (int i = 0; i < S::NLD; ++i) {
-    const int c = tid + i * kThreads;
-    if (S::NCHUNK % kThreads == 0 || c < S::NCHUNK) {
+    const int c = tid + i * S::THREADS;
+    if (S::NCHUNK % S::THREADS == 0 || c < S::NCHUNK) {
       const int row = c / C::ROWCH, part = c - row * C::ROWCH;
       const int key = min(kv0 + row, L - 1);
       const int64_t off = ((int64_t)(s0 + key) * a.H + h) * D + C::CHB * part;
@@ -114,8 +117,8 @@ __device__ __forceinline__ void commit_tile(uint8_t* kb, uint8_t* vb, int tid, c
   using C = Cfg<D>;
 #pragma unroll
   for (int i = 0; i < S::NLD; ++i) {
-    const int c = tid + i * kThreads;
-    if (S::NCHUNK % kThreads == 0 || c < S::NCHUNK) {
+    const int c = tid + i * S::THREADS;
+    if (S::NCHUNK % S::THREADS == 0 || c < S::NCHUNK) {
       const int row = c / C::ROWCH, part = c - row * C::ROWCH;
       *reinterpret_cast<typename S::chunk_t*>(kb + k_row(row) * C::KS + C::CHB * part) = kr[i];
       *reinterpret_cast<typename S::chunk_t*>(vb + v_off<D>(row) + C::CHB * part) = vr[i];
@@ -124,7 +127,6 @@ __device__ __forceinline__ void commit_tile(uint8_t* kb, uint8_t* vb, int tid, c
 }
 
 // A operand of S^T block t: lane row i16 <-> key 32*(i16/4) + 4t + i16%4, d bytes 32g..32g+31.
-typedef int v4i __attribute__((ext_vector_type(4)));
 template <int D>
 __device__ __forceinline__ v8i k_operand(const uint8_t* kb, int t, int g, int i16) {
   const int krow = 16 * t + 4 * (i16 & 3) + (i16 >> 2);   // = k_row(32*(i16/4) + 4t + i16%4)
@@ -167,9 +169,13 @@ __device__ __forceinline__ int2 probs_to_fp8(const v4f& s, float c, float nb) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 72 ? 2 : 1, 2))) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * Cfg<D>::WAVES) __attribute__((amdgpu_waves_per_eu(Cfg<D>::MIN_WAVES_PER_EU)))
+void attn_kernel(AttnArgs a) {
   using C = Cfg<D>;
   using S = Stage<D>;
+  constexpr int QB = C::QB;
+  constexpr int BMW = 16 * QB;
+  static_assert(C::WAVES * BMW == kBM, "block shape");
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[2 * S::KBUF];
   __shared__ __attribute__((aligned(16))) uint8_t v_lds[2 * S::VBUF];
 
@@ -197,7 +203,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 7
   // ---- first K/V tile in flight while the constant parts are written ----
   typename S::chunk_t kr[S::NLD], vr[S::NLD];
   prefetch_tile<D>(a, s0, L, h, 0, tid, kr, vr);
-  for (int r = tid; r < 2 * kBN; r += kThreads) {
+  for (int r = tid; r < 2 * kBN; r += S::THREADS) {
     uint8_t* kr0 = k_lds + (r / kBN) * S::KBUF + (r % kBN) * C::KS;
     uint8_t* vr0 = v_lds + (r / kBN) * S::VBUF + v_off<D>(r % kBN);
 #pragma unroll
@@ -211,11 +217,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 7
   const float cexp = a.softmax_scale * dq * dk * kLog2e;   // raw score -> log2 units (> 0)
 
   // ---- Q operands (B of S^T): lane holds query i16 of its block, d bytes 32g.. ----
-  v8i qop[2];
+  v8i qop[QB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     qop[qb] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    const int qr = q0 + wave * kBMW + qb * 16 + i16;
+    const int qr = q0 + wave * BMW + qb * 16 + i16;
     if (qr < L) {
       const uint8_t* src = a.q8 + ((int64_t)(s0 + qr) * a.H + h) * D;
       if (D == 72) {
@@ -232,20 +238,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 7
           qop[qb][1] = (int)u.y;
         }
       } else {
-        uint4 u0 = *reinterpret_cast<const uint4*>(src + 32 * g);
-        uint4 u1 = *reinterpret_cast<const uint4*>(src + 32 * g + 16);
-        qop[qb] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+        const v4i u0 = *reinterpret_cast<const v4i*>(src + 32 * g);
+        const v4i u1 = *reinterpret_cast<const v4i*>(src + 32 * g + 16);
+        qop[qb] = __builtin_shufflevector(u0, u1, 0, 1, 2, 3, 4, 5, 6, 7);
       }
     }
   }
 
-  v4f o[2][C::NCB];
+  v4f o[QB][C::NCB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int cb = 0; cb < C::NCB; ++cb) o[qb][cb] = v4f{0.f, 0.f, 0.f, 0.f};
-  float mref[2] = {-INFINITY, -INFINITY};   // reference max, log2 units
-  float thr[2] = {-INFINITY, -INFINITY};    // raw-score threshold (m_ref + lazy) / c
+  float mref[QB], thr[QB];   // reference max (log2 units); raw-score threshold (m_ref + lazy) / c
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) mref[qb] = thr[qb] = -INFINITY;
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
 
   commit_tile<D>(k_lds, v_lds, tid, kr, vr);
@@ -255,49 +262,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 7
     const int kv0 = j * kBN;
     const uint8_t* kb = k_lds + (j & 1) * S::KBUF;
     const uint8_t* vb = v_lds + (j & 1) * S::VBUF;
-    if (j + 1 < ntiles) prefetch_tile<D>(a, s0, L, h, kv0 + kBN, tid, kr, vr);
+    const bool has_next = j + 1 < ntiles;
+    if (has_next) prefetch_tile<D>(a, s0, L, h, kv0 + kBN, tid, kr, vr);
     const bool partial = kv0 + kBN > L;
 
-
-    // ---- S^T and P~ per 16-key block, with the running per-lane max ----
-    v8i phi[2], plo[2];
-    float lm[2] = {-INFINITY, -INFINITY};
-    // S^T of block t+1 is issued on the matrix core before the softmax VALU
-    // work of block t, so the two overlap within the wave.
-    const bool has_next = j + 1 < ntiles;
+    // ---- S^T and P~ per 16-key block, with the running per-lane max. S^T of
+    // block t+1 is issued on the matrix core before the VALU work of block t.
+    v8i phi[QB], plo[QB];
+    float lm[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) lm[qb] = -INFINITY;
     auto run_pass = [&](bool commit_here) {
-      const float nb0 = kExpBias - mref[0], nb1 = kExpBias - mref[1];
+      float nb[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) nb[qb] = kExpBias - mref[qb];
       v8i kop = k_operand<D>(kb, 0, g, i16);
-      v4f sa0 = mfma_fp8(kop, qop[0], zero4);
-      v4f sa1 = mfma_fp8(kop, qop[1], zero4);
+      v4f sa[QB], sb[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sa[qb] = mfma_fp8(kop, qop[qb], zero4);
       kop = k_operand<D>(kb, 1, g, i16);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        v4f sb0, sb1;
         if (t + 1 < 8) {
-          sb0 = mfma_fp8(kop, qop[0], zero4);
-          sb1 = mfma_fp8(kop, qop[1], zero4);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) sb[qb] = mfma_fp8(kop, qop[qb], zero4);
           if (t + 2 < 8) kop = k_operand<D>(kb, t + 2, g, i16);
         }
-        if (partial) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const bool oob = kv0 + 32 * g + 4 * t + r >= L;
-            sa0[r] = oob ? -INFINITY : sa0[r];
-            sa1[r] = oob ? -INFINITY : sa1[r];
+        for (int qb = 0; qb < QB; ++qb) {
+          if (partial) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sa[qb][r] = (kv0 + 32 * g + 4 * t + r >= L) ? -INFINITY : sa[qb][r];
           }
-        }
-        lm[0] = fmaxf(fmaxf(fmaxf(fmaxf(lm[0], sa0[0]), sa0[1]), sa0[2]), sa0[3]);
-        lm[1] = fmaxf(fmaxf(fmaxf(fmaxf(lm[1], sa1[0]), sa1[1]), sa1[2]), sa1[3]);
-        const int2 p0 = probs_to_fp8(sa0, cexp, nb0);
-        const int2 p1 = probs_to_fp8(sa1, cexp, nb1);
-        phi[0][t] = p0.x;
-        plo[0][t] = p0.y;
-        phi[1][t] = p1.x;
-        plo[1][t] = p1.y;
-        if (t + 1 < 8) {
-          sa0 = sb0;
-          sa1 = sb1;
+          lm[qb] = fmaxf(fmaxf(fmaxf(fmaxf(lm[qb], sa[qb][0]), sa[qb][1]), sa[qb][2]), sa[qb][3]);
+          const int2 p = probs_to_fp8(sa[qb], cexp, nb[qb]);
+          phi[qb][t] = p.x;
+          plo[qb][t] = p.y;
+          if (t + 1 < 8) sa[qb] = sb[qb];
         }
         // The other buffer is free since the last barrier: store the next
         // tile early so its registers do not stay live through the pass.
@@ -309,9 +310,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 7
     // Overflow check: a score above its row's threshold means P~ may exceed
     // 448. Then reduce the row max over the four lane groups, move the
     // reference max, rescale O and recompute this tile's probabilities.
-    if (__ballot(lm[0] > thr[0] || lm[1] > thr[1]) != 0ull) {
+    bool over = false;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) over = over || (lm[qb] > thr[qb]);
+    if (__ballot(over) != 0ull) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
         float m = lm[qb];
         m = fmaxf(m, __shfl_xor(m, 16, 64));
         m = fmaxf(m, __shfl_xor(m, 32, 64));
@@ -334,7 +338,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 7
                                         : v8i{0, 0, 0, 0, 0, 0, 0, 0})
                           : v_operand<D>(vb, cb, g, i16);
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < QB; ++qb) {
         o[qb][cb] = mfma_fp8(vop, phi[qb], o[qb][cb]);
         o[qb][cb] = mfma_fp8(vop, plo[qb], o[qb][cb]);
       }
@@ -345,10 +349,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 7
 
   // ---- epilogue: divide by the row sum (ones column), scale by dv, bf16 ----
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float lsum = __shfl(o[qb][C::ONES_CB][0], C::ONES_LANE0 + i16, 64);
     const float f = dv / lsum;
-    const int qr = q0 + wave * kBMW + qb * 16 + i16;
+    const int qr = q0 + wave * BMW + qb * 16 + i16;
     if (qr < L) {
       uint16_t* dst = a.out + (int64_t)(s0 + qr) * a.ld_out + (int64_t)h * D;
 #pragma unroll
@@ -374,9 +378,9 @@ hipError_t launch_attn(const AttnArgs& a, int head_dim, int total_tokens, hipStr
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   (void)total_tokens;
   if (head_dim == 72)
-    hipLaunchKernelGGL(attn_kernel<72>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(attn_kernel<72>, dim3((unsigned)grid), dim3(64 * Cfg<72>::WAVES), 0, s, a);
   else
-    hipLaunchKernelGGL(attn_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(attn_kernel<128>, dim3((unsigned)grid), dim3(64 * Cfg<128>::WAVES), 0, s, a);
   return hipGetLastError();
 }
 
