@@ -91,7 +91,7 @@ fp8vit_status fp8vit_attn_varlen(const void* q8, const void* k8, const void* v8,
       !aligned(d_state, 256))
     return FP8VIT_ERR_UNSUPPORTED;
   if (num_segments == 0 || total_tokens == 0 || max_seqlen == 0) return FP8VIT_OK;  // no rows to write
-  const int bm = fp8vit::attn_block_m();
+  const int bm = fp8vit::attn_block_m(head_dim);
   const int64_t by_total = ((int64_t)total_tokens + bm - 1) / bm + num_segments;
   const int64_t by_max = (int64_t)num_segments * (((int64_t)max_seqlen + bm - 1) / bm);
   const int64_t ntiles = by_total < by_max ? by_total : by_max;

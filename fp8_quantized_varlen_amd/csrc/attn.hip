@@ -46,7 +46,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 
-constexpr int kBM = 128;             // queries per workgroup
 constexpr int kBN = 128;             // keys per tile
 constexpr float kExpBias = 7.0f;     // P~ = 2^7 * exp2(t - m_ref)
 constexpr float kLazy = 1.75f;       // log2 growth of the max tolerated before rescaling
@@ -55,13 +54,17 @@ constexpr float kLog2e = 1.4426950408889634f;
 template <int D> struct Cfg;
 // KS/VS: LDS row strides in bytes. NCB: 16-column blocks of O^T including the
 // ones column. CHB x ROWCH: bytes per global load x loads per K/V row.
+// WAVES x QB x 16 = BM queries per workgroup.
+// hd72: K rows are 80 bytes (72 + 8 zero bytes); the d-padding lanes of the
+// S^T operand read past their row into the next one, which only meets the
+// zero bytes of the Q operand, or read a 32-byte zero block after the tile.
 template <> struct Cfg<72> {
-  static constexpr int KS = 112, VS = 80, NCB = 5, CHB = 8, ROWCH = 9, ONES_CB = 4, ONES_LANE0 = 32;
-  static constexpr int WAVES = 8, QB = 1, MIN_WAVES_PER_EU = 4;
+  static constexpr int KS = 80, VS = 80, NCB = 5, CHB = 8, ROWCH = 9, ONES_CB = 4, ONES_LANE0 = 32;
+  static constexpr int WAVES = 4, QB = 1, MIN_WAVES_PER_EU = 3, BM = 64;
 };
 template <> struct Cfg<128> {
   static constexpr int KS = 144, VS = 144, NCB = 9, CHB = 16, ROWCH = 8, ONES_CB = 8, ONES_LANE0 = 0;
-  static constexpr int WAVES = 8, QB = 1, MIN_WAVES_PER_EU = 2;
+  static constexpr int WAVES = 8, QB = 1, MIN_WAVES_PER_EU = 2, BM = 128;
 };
 
 // LDS placement of a tile's rows.
@@ -77,7 +80,8 @@ template <int D> struct Stage {
   static constexpr int THREADS = 64 * Cfg<D>::WAVES;
   static constexpr int NCHUNK = kBN * Cfg<D>::ROWCH;                    // chunks per tensor and tile
   static constexpr int NLD = (NCHUNK + THREADS - 1) / THREADS;          // per thread
-  static constexpr int KBUF = kBN * Cfg<D>::KS, VBUF = kBN * Cfg<D>::VS + 64 * (kBN / 32 - 1);
+  static constexpr int KZERO = kBN * Cfg<D>::KS;                       // 32-byte zero block after the rows
+  static constexpr int KBUF = KZERO + 32, VBUF = kBN * Cfg<D>::VS + 64 * (kBN / 32 - 1);
   using chunk_t = typename std::conditional<Cfg<D>::CHB == 8, u32x2, u32x4>::type;
 };
 
@@ -130,8 +134,10 @@ __device__ __forceinline__ void commit_tile(uint8_t* kb, uint8_t* vb, int tid, c
 template <int D>
 __device__ __forceinline__ v8i k_operand(const uint8_t* kb, int t, int g, int i16) {
   const int krow = 16 * t + 4 * (i16 & 3) + (i16 >> 2);   // = k_row(32*(i16/4) + 4t + i16%4)
-  const int koff = (D == 72 && g == 3) ? 80 : 32 * g;     // hd72: bytes 72..111 of a row are zero
-  const uint8_t* kp = kb + krow * Cfg<D>::KS + koff;
+  // hd72: lane group 3 holds only d-padding -> zero block; group 2 reads
+  // bytes 64..95 (8 data bytes, 8 zero bytes, 16 bytes of the next row that
+  // multiply zeros of Q).
+  const uint8_t* kp = (D == 72 && g == 3) ? kb + Stage<D>::KZERO : kb + krow * Cfg<D>::KS + 32 * g;
   const v4i k0 = *reinterpret_cast<const v4i*>(kp);
   const v4i k1 = *reinterpret_cast<const v4i*>(kp + 16);
   return __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -175,9 +181,10 @@ void attn_kernel(AttnArgs a) {
   using S = Stage<D>;
   constexpr int QB = C::QB;
   constexpr int BMW = 16 * QB;
+  constexpr int kBM = C::BM;
   static_assert(C::WAVES * BMW == kBM, "block shape");
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[2 * S::KBUF];
-  __shared__ __attribute__((aligned(16))) uint8_t v_lds[2 * S::VBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds[3 * S::VBUF];
 
   // ---- work item: XCD-grouped (head, query tile) -> segment by prefix scan ----
   const int G = gridDim.x;
@@ -203,13 +210,20 @@ void attn_kernel(AttnArgs a) {
   // ---- first K/V tile in flight while the constant parts are written ----
   typename S::chunk_t kr[S::NLD], vr[S::NLD];
   prefetch_tile<D>(a, s0, L, h, 0, tid, kr, vr);
-  for (int r = tid; r < 2 * kBN; r += S::THREADS) {
-    uint8_t* kr0 = k_lds + (r / kBN) * S::KBUF + (r % kBN) * C::KS;
+  for (int r = tid; r < 2 * (kBN + 4); r += S::THREADS) {
+    uint8_t* kr0 = k_lds + (r / (kBN + 4)) * S::KBUF;
+    const int rr = r % (kBN + 4);
+    if (rr < kBN) {
+#pragma unroll
+      for (int b = D; b < C::KS; b += 8) *reinterpret_cast<uint2*>(kr0 + rr * C::KS + b) = make_uint2(0u, 0u);
+    } else {
+      *reinterpret_cast<uint2*>(kr0 + S::KZERO + 8 * (rr - kBN)) = make_uint2(0u, 0u);
+    }
+  }
+  for (int r = tid; r < 3 * kBN; r += S::THREADS) {
     uint8_t* vr0 = v_lds + (r / kBN) * S::VBUF + v_off<D>(r % kBN);
 #pragma unroll
-    for (int b = D; b < C::KS; b += 8) *reinterpret_cast<uint2*>(kr0 + b) = make_uint2(0u, 0u);
-#pragma unroll
-    for (int b = D; b < C::VS; b += 8)
+    for (int b = 0; b < C::VS; b += 8)
       *reinterpret_cast<uint2*>(vr0 + b) = make_uint2((D == 72 && b == 72) ? 0x38u : 0u, 0u);
   }
 
@@ -255,96 +269,133 @@ void attn_kernel(AttnArgs a) {
   for (int qb = 0; qb < QB; ++qb) mref[qb] = thr[qb] = -INFINITY;
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
 
+  __syncthreads();   // zero fill above overlaps the rows stored next
   commit_tile<D>(k_lds, v_lds, tid, kr, vr);
   __syncthreads();
 
-  for (int j = 0; j < ntiles; ++j) {
+  // P of the previous tile: its O^T += V^T P^T products are interleaved with
+  // the softmax VALU work of the current tile (matrix core and VALU overlap
+  // inside each wave). V is triple-buffered so that the previous tile's V
+  // stays in LDS while the next one is being stored. Before the first tile the
+  // "previous" P is zero and its V buffer holds zeros, so the products add 0.
+  v8i phi_prev[QB], plo_prev[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) phi_prev[qb] = plo_prev[qb] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  const v8i ones_op = (i16 == 0) ? v8i{0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                                       0x38383838, 0x38383838}
+                                 : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  auto pv_block = [&](const uint8_t* vbp, int cb) {
+    const v8i vop = (D == 128 && cb == 8) ? ones_op : v_operand<D>(vbp, cb, g, i16);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      o[qb][cb] = mfma_fp8(vop, phi_prev[qb], o[qb][cb]);
+      o[qb][cb] = mfma_fp8(vop, plo_prev[qb], o[qb][cb]);
+    }
+  };
+
+  // One pass over the 8 S^T blocks of a tile. Template flags keep the
+  // unrolled body free of branches: PARTIAL masks keys past the segment end
+  // (last tile only), WITH_PV interleaves the previous tile's P.V, COMMIT
+  // stores the prefetched next tile after block 3.
+  v8i phi[QB], plo[QB];
+  float lm[QB];
+  auto run_pass = [&](auto partial_c, auto pv_c, auto commit_c, int j) {
+    constexpr bool PARTIAL = decltype(partial_c)::value;
+    constexpr bool WITH_PV = decltype(pv_c)::value;
+    constexpr bool COMMIT = decltype(commit_c)::value;
     const int kv0 = j * kBN;
     const uint8_t* kb = k_lds + (j & 1) * S::KBUF;
-    const uint8_t* vb = v_lds + (j & 1) * S::VBUF;
-    const bool has_next = j + 1 < ntiles;
-    if (has_next) prefetch_tile<D>(a, s0, L, h, kv0 + kBN, tid, kr, vr);
-    const bool partial = kv0 + kBN > L;
-
-    // ---- S^T and P~ per 16-key block, with the running per-lane max. S^T of
-    // block t+1 is issued on the matrix core before the VALU work of block t.
-    v8i phi[QB], plo[QB];
-    float lm[QB];
+    const uint8_t* vprev = v_lds + ((j + 2) % 3) * S::VBUF;   // V of tile j-1
+    float nb[QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) lm[qb] = -INFINITY;
-    auto run_pass = [&](bool commit_here) {
-      float nb[QB];
+    for (int qb = 0; qb < QB; ++qb) {
+      nb[qb] = kExpBias - mref[qb];
+      lm[qb] = -INFINITY;
+    }
+    v8i kop = k_operand<D>(kb, 0, g, i16);
+    v4f sa[QB], sb[QB];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) nb[qb] = kExpBias - mref[qb];
-      v8i kop = k_operand<D>(kb, 0, g, i16);
-      v4f sa[QB], sb[QB];
+    for (int qb = 0; qb < QB; ++qb) sa[qb] = mfma_fp8(kop, qop[qb], zero4);
+    kop = k_operand<D>(kb, 1, g, i16);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sa[qb] = mfma_fp8(kop, qop[qb], zero4);
-      kop = k_operand<D>(kb, 1, g, i16);
+    for (int t = 0; t < 8; ++t) {
+      if (t + 1 < 8) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        if (t + 1 < 8) {
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) sb[qb] = mfma_fp8(kop, qop[qb], zero4);
-          if (t + 2 < 8) kop = k_operand<D>(kb, t + 2, g, i16);
-        }
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          if (partial) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sa[qb][r] = (kv0 + 32 * g + 4 * t + r >= L) ? -INFINITY : sa[qb][r];
-          }
-          lm[qb] = fmaxf(fmaxf(fmaxf(fmaxf(lm[qb], sa[qb][0]), sa[qb][1]), sa[qb][2]), sa[qb][3]);
-          const int2 p = probs_to_fp8(sa[qb], cexp, nb[qb]);
-          phi[qb][t] = p.x;
-          plo[qb][t] = p.y;
-          if (t + 1 < 8) sa[qb] = sb[qb];
-        }
-        // The other buffer is free since the last barrier: store the next
-        // tile early so its registers do not stay live through the pass.
-        if (t == 3 && commit_here && has_next)
-          commit_tile<D>(k_lds + ((j + 1) & 1) * S::KBUF, v_lds + ((j + 1) & 1) * S::VBUF, tid, kr, vr);
+        for (int qb = 0; qb < QB; ++qb) sb[qb] = mfma_fp8(kop, qop[qb], zero4);
+        if (t + 2 < 8) kop = k_operand<D>(kb, t + 2, g, i16);
       }
-    };
-    run_pass(true);
-    // Overflow check: a score above its row's threshold means P~ may exceed
-    // 448. Then reduce the row max over the four lane groups, move the
-    // reference max, rescale O and recompute this tile's probabilities.
+      if (WITH_PV) {                     // one 16-column block per 16-key block
+        if (t < C::NCB) pv_block(vprev, t);
+        if (t == 7 && C::NCB > 8) pv_block(vprev, 8);
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        if (PARTIAL) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sa[qb][r] = (kv0 + 32 * g + 4 * t + r >= L) ? -INFINITY : sa[qb][r];
+        }
+        lm[qb] = fmaxf(fmaxf(fmaxf(fmaxf(lm[qb], sa[qb][0]), sa[qb][1]), sa[qb][2]), sa[qb][3]);
+        const int2 p = probs_to_fp8(sa[qb], cexp, nb[qb]);
+        phi[qb][t] = p.x;
+        plo[qb][t] = p.y;
+        if (t + 1 < 8) sa[qb] = sb[qb];
+      }
+      // The buffers of the next tile are free since the last barrier: store
+      // it early so its registers do not stay live through the pass.
+      if (COMMIT && t == 3)
+        commit_tile<D>(k_lds + ((j + 1) & 1) * S::KBUF, v_lds + ((j + 1) % 3) * S::VBUF, tid, kr, vr);
+    }
+  };
+  // Overflow check after a pass: a score above its row's threshold means P~
+  // may exceed 448. Then reduce the row max over the four lane groups, move
+  // the reference max, rescale O (which holds every earlier tile by now) and
+  // recompute this tile's probabilities.
+  auto need_redo = [&]() {
     bool over = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) over = over || (lm[qb] > thr[qb]);
-    if (__ballot(over) != 0ull) {
+    if (__ballot(over) == 0ull) return false;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float m = lm[qb];
-        m = fmaxf(m, __shfl_xor(m, 16, 64));
-        m = fmaxf(m, __shfl_xor(m, 32, 64));
-        const float mn = fmaxf(mref[qb], m * cexp);
-        const float alpha = __builtin_amdgcn_exp2f(mref[qb] - mn);
-        mref[qb] = mn;
-        thr[qb] = (mn + kLazy) / cexp;
+    for (int qb = 0; qb < QB; ++qb) {
+      float m = lm[qb];
+      m = fmaxf(m, __shfl_xor(m, 16, 64));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      const float mn = fmaxf(mref[qb], m * cexp);
+      const float alpha = __builtin_amdgcn_exp2f(mref[qb] - mn);
+      mref[qb] = mn;
+      thr[qb] = (mn + kLazy) / cexp;
 #pragma unroll
-        for (int cb = 0; cb < C::NCB; ++cb) o[qb][cb] *= alpha;
-      }
-      run_pass(false);
+      for (int cb = 0; cb < C::NCB; ++cb) o[qb][cb] *= alpha;
     }
-
-    // ---- O^T += V^T P^T (hi and lo terms) ----
+    return true;
+  };
+  auto shift_p = [&]() {
 #pragma unroll
-    for (int cb = 0; cb < C::NCB; ++cb) {
-      const v8i vop = (D == 128 && cb == 8)
-                          ? ((i16 == 0) ? v8i{0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                                              0x38383838, 0x38383838, 0x38383838}
-                                        : v8i{0, 0, 0, 0, 0, 0, 0, 0})
-                          : v_operand<D>(vb, cb, g, i16);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        o[qb][cb] = mfma_fp8(vop, phi[qb], o[qb][cb]);
-        o[qb][cb] = mfma_fp8(vop, plo[qb], o[qb][cb]);
-      }
+    for (int qb = 0; qb < QB; ++qb) {
+      phi_prev[qb] = phi[qb];
+      plo_prev[qb] = plo[qb];
     }
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
 
+  // full tiles
+  for (int j = 0; j + 1 < ntiles; ++j) {
+    prefetch_tile<D>(a, s0, L, h, (j + 1) * kBN, tid, kr, vr);
+    run_pass(F_{}, T_{}, T_{}, j);
+    if (need_redo()) run_pass(F_{}, F_{}, F_{}, j);
+    shift_p();
     __syncthreads();
+  }
+  // last tile (keys past the segment end masked), then its own P.V
+  {
+    const int j = ntiles - 1;
+    run_pass(T_{}, T_{}, F_{}, j);
+    if (need_redo()) run_pass(T_{}, F_{}, F_{}, j);
+    shift_p();
+    const uint8_t* vlast = v_lds + (j % 3) * S::VBUF;
+#pragma unroll
+    for (int cb = 0; cb < C::NCB; ++cb) pv_block(vlast, cb);
   }
 
   // ---- epilogue: divide by the row sum (ones column), scale by dv, bf16 ----
@@ -370,7 +421,7 @@ void attn_kernel(AttnArgs a) {
   }
 }
 
-int attn_block_m() { return kBM; }
+int attn_block_m(int head_dim) { return head_dim == 72 ? Cfg<72>::BM : Cfg<128>::BM; }
 
 hipError_t launch_attn(const AttnArgs& a, int head_dim, int total_tokens, hipStream_t s) {
   const int64_t items = (int64_t)a.H * a.ntiles_ub;

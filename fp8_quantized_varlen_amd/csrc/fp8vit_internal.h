@@ -58,6 +58,6 @@ struct AttnArgs {
   float softmax_scale;
 };
 hipError_t launch_attn(const AttnArgs& a, int head_dim, int total_tokens, hipStream_t s);
-int attn_block_m();
+int attn_block_m(int head_dim);
 
 }  // namespace fp8vit
