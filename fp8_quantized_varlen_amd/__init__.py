@@ -5,8 +5,9 @@ Argument marshalling only: every step of the hot path (amax, scale
 bookkeeping, e4m3 quantization, varlen attention) runs in the library's HIP
 kernels. PyTorch supplies device memory and the current stream.
 
-If the shared library has not been built, importing this package raises
-ImportError: there is no CPU fallback.
+If the shared library has not been built, the first call raises
+ImportError: there is no CPU fallback. (Importing the package itself works
+without it, so that the build module can run.)
 """
 from __future__ import annotations
 
@@ -26,12 +27,6 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8vit.s
 FP8VIT_DYNAMIC = 0
 FP8VIT_STATIC = 1
 _MODES = {"dynamic": FP8VIT_DYNAMIC, "static": FP8VIT_STATIC}
-
-if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m fp8_quantized_varlen_amd.build` "
-                      "(the HIP library is required; there is no fallback path)")
-_lib = ctypes.CDLL(LIB_PATH)
-
 
 class _StateView(ctypes.Structure):
     _fields_ = [("ring", (ctypes.c_float * 16) * 3), ("count", ctypes.c_uint32),
@@ -53,10 +48,31 @@ _SIGS = {
     "fp8vit_state_read": (ctypes.c_int, [_vp, ctypes.POINTER(_StateView), _vp]),
     "fp8vit_status_str": (ctypes.c_char_p, [ctypes.c_int]),
 }
-for _name, (_res, _args) in _SIGS.items():
-    _fn = getattr(_lib, _name)
-    _fn.restype = _res
-    _fn.argtypes = _args
+_LIB = None
+
+
+def _lib_handle():
+    """Load libfp8vit.so on first use; raise ImportError if it was never built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m fp8_quantized_varlen_amd.build` "
+                              "(the HIP library is required; there is no fallback path)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+class _Lazy:
+    def __getattr__(self, name):
+        return getattr(_lib_handle(), name)
+
+
+_lib = _Lazy()
 
 EXPORTED_SYMBOLS = tuple(_SIGS)
 

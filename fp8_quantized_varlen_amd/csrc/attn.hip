@@ -45,6 +45,8 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
+typedef __attribute__((address_space(3))) v4i lds_v4i;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 constexpr int kBN = 128;             // keys per tile
 constexpr float kExpBias = 7.0f;     // P~ = 2^7 * exp2(t - m_ref)
@@ -78,9 +80,15 @@ template <int D> __device__ __forceinline__ int v_off(int key) { return key * Cf
 
 template <int D> struct Stage {
   static constexpr int THREADS = 64 * Cfg<D>::WAVES;
-  static constexpr int NCHUNK = kBN * Cfg<D>::ROWCH;                    // chunks per tensor and tile
-  static constexpr int NLD = (NCHUNK + THREADS - 1) / THREADS;          // per thread
-  static constexpr int KZERO = kBN * Cfg<D>::KS;                       // 32-byte zero block after the rows
+  // Staging: TPR threads per K/V row, each moving CPT chunks starting at
+  // chunk P0_STEP * (tid % TPR) (neighbours may overlap by a chunk; both then
+  // store the same bytes).
+  static constexpr int TPR = THREADS / kBN;
+  static constexpr int CPT = (Cfg<D>::ROWCH + TPR - 1) / TPR;
+  static constexpr int P0_STEP = TPR > 1 ? (Cfg<D>::ROWCH - CPT) / (TPR - 1) : 0;
+  static_assert(TPR >= 1 && THREADS % kBN == 0, "staging shape");
+  static_assert(P0_STEP * (TPR - 1) + CPT == Cfg<D>::ROWCH && P0_STEP <= CPT, "staging covers each row");
+  static constexpr int KZERO = kBN * Cfg<D>::KS;                       // 32 bytes after the rows
   static constexpr int KBUF = KZERO + 32, VBUF = kBN * Cfg<D>::VS + 64 * (kBN / 32 - 1);
   using chunk_t = typename std::conditional<Cfg<D>::CHB == 8, u32x2, u32x4>::type;
 };
@@ -94,63 +102,63 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Global -> register prefetch of one K/V tile (rows past the segment end read
-// the last valid row: those keys are masked or multiplied by P = 0).
+// Global -> register prefetch of this thread's chunks of one K/V row of a
+// tile. Rows past the segment end read the last valid row: those keys are
+// masked or multiplied by P = 0. kg/vg point at this thread's first chunk of
+// key 0 of the segment for this head.
 template <int D>
-__device__ __forceinline__ void prefetch_tile(const AttnArgs& a, int s0, int L, int h, int kv0, int tid,
-                                              typename Stage<D>::chunk_t* kr, typename Stage<D>::chunk_t* vr) {
+__device__ __forceinline__ void prefetch_row(const uint8_t* kg, const uint8_t* vg, uint32_t row_stride, int key,
+                                             typename Stage<D>::chunk_t* kr, typename Stage<D>::chunk_t* vr) {
   using S = Stage<D>;
-  using C = Cfg<D>;
+  const uint32_t off = (uint32_t)key * row_stride;
 #pragma unroll
-  for (int i = 0; i < S::NLD; ++i) {
-    const int c = tid + i * S::THREADS;
-    if (S::NCHUNK % S::THREADS == 0 || c < S::NCHUNK) {
-      const int row = c / C::ROWCH, part = c - row * C::ROWCH;
-      const int key = min(kv0 + row, L - 1);
-      const int64_t off = ((int64_t)(s0 + key) * a.H + h) * D + C::CHB * part;
-      kr[i] = *reinterpret_cast<const typename S::chunk_t*>(a.k8 + off);
-      vr[i] = *reinterpret_cast<const typename S::chunk_t*>(a.v8 + off);
-    }
+  for (int i = 0; i < S::CPT; ++i) {
+    kr[i] = *reinterpret_cast<const typename S::chunk_t*>(kg + off + Cfg<D>::CHB * i);
+    vr[i] = *reinterpret_cast<const typename S::chunk_t*>(vg + off + Cfg<D>::CHB * i);
   }
 }
 
 template <int D>
-__device__ __forceinline__ void commit_tile(uint8_t* kb, uint8_t* vb, int tid, const typename Stage<D>::chunk_t* kr,
-                                            const typename Stage<D>::chunk_t* vr) {
+__device__ __forceinline__ void commit_row(uint8_t* kdst, uint8_t* vdst, const typename Stage<D>::chunk_t* kr,
+                                           const typename Stage<D>::chunk_t* vr) {
   using S = Stage<D>;
-  using C = Cfg<D>;
 #pragma unroll
-  for (int i = 0; i < S::NLD; ++i) {
-    const int c = tid + i * S::THREADS;
-    if (S::NCHUNK % S::THREADS == 0 || c < S::NCHUNK) {
-      const int row = c / C::ROWCH, part = c - row * C::ROWCH;
-      *reinterpret_cast<typename S::chunk_t*>(kb + k_row(row) * C::KS + C::CHB * part) = kr[i];
-      *reinterpret_cast<typename S::chunk_t*>(vb + v_off<D>(row) + C::CHB * part) = vr[i];
-    }
+  for (int i = 0; i < S::CPT; ++i) {
+    *reinterpret_cast<typename S::chunk_t*>(kdst + Cfg<D>::CHB * i) = kr[i];
+    *reinterpret_cast<typename S::chunk_t*>(vdst + Cfg<D>::CHB * i) = vr[i];
   }
 }
 
-// A operand of S^T block t: lane row i16 <-> key 32*(i16/4) + 4t + i16%4, d bytes 32g..32g+31.
+// A operand of S^T block t: lane row i16 <-> key 32*(i16/4) + 4t + i16%4, d bytes
+// 32g..32g+31. `kl` is the lane's byte offset for t = 0 (k_lane_offset); block t
+// adds 16 rows. hd72: lane groups 2 and 3 read bytes 64..95 (8 data bytes, then
+// bytes that only meet zero bytes of the Q operand).
 template <int D>
-__device__ __forceinline__ v8i k_operand(const uint8_t* kb, int t, int g, int i16) {
-  const int krow = 16 * t + 4 * (i16 & 3) + (i16 >> 2);   // = k_row(32*(i16/4) + 4t + i16%4)
-  // hd72: lane group 3 holds only d-padding -> zero block; group 2 reads
-  // bytes 64..95 (8 data bytes, 8 zero bytes, 16 bytes of the next row that
-  // multiply zeros of Q).
-  const uint8_t* kp = (D == 72 && g == 3) ? kb + Stage<D>::KZERO : kb + krow * Cfg<D>::KS + 32 * g;
-  const v4i k0 = *reinterpret_cast<const v4i*>(kp);
-  const v4i k1 = *reinterpret_cast<const v4i*>(kp + 16);
+__device__ __forceinline__ int k_lane_offset(int g, int i16) {
+  const int krow = 4 * (i16 & 3) + (i16 >> 2);            // = k_row(32*(i16/4) + i16%4)
+  return krow * Cfg<D>::KS + (D == 72 ? min(32 * g, 64) : 32 * g);
+}
+template <int D>
+__device__ __forceinline__ v8i k_operand(const lds_u8* kl, int t) {
+  const lds_u8* kp = kl + 16 * t * Cfg<D>::KS;
+  const v4i k0 = *(const lds_v4i*)(kp);
+  const v4i k1 = *(const lds_v4i*)(kp + 16);
   return __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // A operand of O^T block cb: lane row i16 <-> V column 16cb + i16, keys 32g..32g+31,
-// gathered from row-major V by the byte-transposing LDS read.
+// gathered from row-major V by the byte-transposing LDS read. `vl` is the lane's
+// byte offset (v_lane_offset); the 8-key steps and the column block are constants.
 template <int D>
-__device__ __forceinline__ v8i v_operand(const uint8_t* vb, int cb, int g, int i16) {
+__device__ __forceinline__ int v_lane_offset(int g, int i16) {
+  return v_off<D>(32 * g + (i16 >> 1)) + 8 * (i16 & 1);
+}
+template <int D>
+__device__ __forceinline__ v8i v_operand(const lds_u8* vl, int cb) {
   v8i r;
 #pragma unroll
   for (int sidx = 0; sidx < 4; ++sidx) {
-    const uint8_t* vp = vb + v_off<D>(32 * g + 8 * sidx + (i16 >> 1)) + 16 * cb + 8 * (i16 & 1);
+    const lds_u8* vp = vl + 8 * sidx * Cfg<D>::VS + 16 * cb;
     const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vp));
     r[2 * sidx] = x[0];
     r[2 * sidx + 1] = x[1];
@@ -207,9 +215,17 @@ void attn_kernel(AttnArgs a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, i16 = lane & 15;
 
-  // ---- first K/V tile in flight while the constant parts are written ----
-  typename S::chunk_t kr[S::NLD], vr[S::NLD];
-  prefetch_tile<D>(a, s0, L, h, 0, tid, kr, vr);
+  // ---- staging geometry; first K/V tile in flight while the constants are written ----
+  const int srow = tid / S::TPR;
+  const int schunk = S::P0_STEP * (tid % S::TPR);
+  const uint32_t row_stride = (uint32_t)a.H * D;
+  const int64_t seg_off = ((int64_t)s0 * a.H + h) * D + Cfg<D>::CHB * schunk;
+  const uint8_t* kg = a.k8 + seg_off;
+  const uint8_t* vg = a.v8 + seg_off;
+  const int k_stage = k_row(srow) * C::KS + Cfg<D>::CHB * schunk;   // LDS offsets within a buffer
+  const int v_stage = v_off<D>(srow) + Cfg<D>::CHB * schunk;
+  typename S::chunk_t kr[S::CPT], vr[S::CPT];
+  prefetch_row<D>(kg, vg, row_stride, min(srow, L - 1), kr, vr);
   for (int r = tid; r < 2 * (kBN + 4); r += S::THREADS) {
     uint8_t* kr0 = k_lds + (r / (kBN + 4)) * S::KBUF;
     const int rr = r % (kBN + 4);
@@ -270,8 +286,10 @@ void attn_kernel(AttnArgs a) {
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
 
   __syncthreads();   // zero fill above overlaps the rows stored next
-  commit_tile<D>(k_lds, v_lds, tid, kr, vr);
+  commit_row<D>(k_lds + k_stage, v_lds + v_stage, kr, vr);
   __syncthreads();
+  const int kl_lane = k_lane_offset<D>(g, i16);
+  const int vl_lane = v_lane_offset<D>(g, i16);
 
   // P of the previous tile: its O^T += V^T P^T products are interleaved with
   // the softmax VALU work of the current tile (matrix core and VALU overlap
@@ -284,8 +302,8 @@ void attn_kernel(AttnArgs a) {
   const v8i ones_op = (i16 == 0) ? v8i{0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838,
                                        0x38383838, 0x38383838}
                                  : v8i{0, 0, 0, 0, 0, 0, 0, 0};
-  auto pv_block = [&](const uint8_t* vbp, int cb) {
-    const v8i vop = (D == 128 && cb == 8) ? ones_op : v_operand<D>(vbp, cb, g, i16);
+  auto pv_block = [&](const lds_u8* vbp, int cb) {
+    const v8i vop = (D == 128 && cb == 8) ? ones_op : v_operand<D>(vbp, cb);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       o[qb][cb] = mfma_fp8(vop, phi_prev[qb], o[qb][cb]);
@@ -304,25 +322,31 @@ void attn_kernel(AttnArgs a) {
     constexpr bool WITH_PV = decltype(pv_c)::value;
     constexpr bool COMMIT = decltype(commit_c)::value;
     const int kv0 = j * kBN;
-    const uint8_t* kb = k_lds + (j & 1) * S::KBUF;
-    const uint8_t* vprev = v_lds + ((j + 2) % 3) * S::VBUF;   // V of tile j-1
+    // One base register per operand and tile; the per-block steps become
+    // immediate offsets of the LDS reads (the empty asm keeps the compiler
+    // from hoisting one precomputed address per read out of the loop).
+    uint32_t kbase = (uint32_t)((j & 1) * S::KBUF + kl_lane);
+    uint32_t vbase = (uint32_t)(((j + 2) % 3) * S::VBUF + vl_lane);
+    asm volatile("" : "+v"(kbase), "+v"(vbase));
+    const lds_u8* kl = (const lds_u8*)k_lds + kbase;
+    const lds_u8* vprev = (const lds_u8*)v_lds + vbase;   // V of tile j-1
     float nb[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       nb[qb] = kExpBias - mref[qb];
       lm[qb] = -INFINITY;
     }
-    v8i kop = k_operand<D>(kb, 0, g, i16);
+    v8i kop = k_operand<D>(kl, 0);
     v4f sa[QB], sb[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) sa[qb] = mfma_fp8(kop, qop[qb], zero4);
-    kop = k_operand<D>(kb, 1, g, i16);
+    kop = k_operand<D>(kl, 1);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       if (t + 1 < 8) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) sb[qb] = mfma_fp8(kop, qop[qb], zero4);
-        if (t + 2 < 8) kop = k_operand<D>(kb, t + 2, g, i16);
+        if (t + 2 < 8) kop = k_operand<D>(kl, t + 2);
       }
       if (WITH_PV) {                     // one 16-column block per 16-key block
         if (t < C::NCB) pv_block(vprev, t);
@@ -343,7 +367,7 @@ void attn_kernel(AttnArgs a) {
       // The buffers of the next tile are free since the last barrier: store
       // it early so its registers do not stay live through the pass.
       if (COMMIT && t == 3)
-        commit_tile<D>(k_lds + ((j + 1) & 1) * S::KBUF, v_lds + ((j + 1) % 3) * S::VBUF, tid, kr, vr);
+        commit_row<D>(k_lds + ((j + 1) & 1) * S::KBUF + k_stage, v_lds + ((j + 1) % 3) * S::VBUF + v_stage, kr, vr);
     }
   };
   // Overflow check after a pass: a score above its row's threshold means P~
@@ -351,6 +375,10 @@ void attn_kernel(AttnArgs a) {
   // the reference max, rescale O (which holds every earlier tile by now) and
   // recompute this tile's probabilities.
   auto need_redo = [&]() {
+    // Keep the pass' probabilities computed here, interleaved with its MFMAs,
+    // rather than sunk past the branch into the common path.
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) asm volatile("" : "+v"(phi[qb]), "+v"(plo[qb]));
     bool over = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) over = over || (lm[qb] > thr[qb]);
@@ -381,7 +409,7 @@ void attn_kernel(AttnArgs a) {
 
   // full tiles
   for (int j = 0; j + 1 < ntiles; ++j) {
-    prefetch_tile<D>(a, s0, L, h, (j + 1) * kBN, tid, kr, vr);
+    prefetch_row<D>(kg, vg, row_stride, min((j + 1) * kBN + srow, L - 1), kr, vr);
     run_pass(F_{}, T_{}, T_{}, j);
     if (need_redo()) run_pass(F_{}, F_{}, F_{}, j);
     shift_p();
@@ -393,7 +421,7 @@ void attn_kernel(AttnArgs a) {
     run_pass(T_{}, T_{}, F_{}, j);
     if (need_redo()) run_pass(T_{}, F_{}, F_{}, j);
     shift_p();
-    const uint8_t* vlast = v_lds + (j % 3) * S::VBUF;
+    const lds_u8* vlast = (const lds_u8*)v_lds + (j % 3) * S::VBUF + vl_lane;
 #pragma unroll
     for (int cb = 0; cb < C::NCB; ++cb) pv_block(vlast, cb);
   }
