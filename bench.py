@@ -17,6 +17,7 @@ Prints one JSON line (rank 0). Only one GPU is used: --gpus above 1 exits.
 import argparse
 import json
 import os
+import re
 import sys
 import tempfile
 import time
@@ -44,7 +45,9 @@ def parse():
     p.add_argument("--rotate-mb", type=float, default=600.0,
                    help="cycle through input copies totalling at least this many MB (defeats the 256 MB MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=2048, help="query rows per head in the CPU oracle sample")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle baseline")
+    p.add_argument("--static-values", default=None,
+                   help="q,k,v static values to use instead of calibrating (profiling runs: no dynamic passes)")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 256 MiB device copy (for scaling HBM byte counters)")
     return p.parse_args()
@@ -76,11 +79,13 @@ def calibrate_static(fv, w, dev, margin=1.5):
     return [float(x) for x in loaded]
 
 
-def cpu_baseline(w, qb, kb, vb, static_values, rows_per_head):
-    """The oracle, untuned, on a bounded sample of the same step: quantization of
-    all three tensors in full, fp64 attention for the first `rows_per_head` query
-    rows of every segment and head; the step time is extrapolated linearly in
-    the number of query rows."""
+def cpu_baseline(w, qb, kb, vb, static_values, out_gpu, target_s, compare=True):
+    """The oracle, untuned, timed on this host: oracle quantization of Q, K and V
+    plus fp64 oracle attention. Whole steps are repeated until about `target_s`
+    seconds of CPU work are done; a workload whose single step would take more
+    than 30 s is sampled instead (the first rows of every segment and head, all
+    keys), its step time extrapolated linearly in query rows. The oracle rows
+    computed here are also compared with the GPU output of the same input."""
     import numpy as np
     import oracle
     try:
@@ -88,30 +93,89 @@ def cpu_baseline(w, qb, kb, vb, static_values, rows_per_head):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = os.cpu_count()
-    ring = oracle.scales.AmaxRing()
+    H, d = qb.shape[1], qb.shape[2]
+    sigma = np.float64(oracle.attention.default_softmax_scale(d))
+    cu = [int(x) for x in w.cu_seqlens]
+    segs = [(cu[i], cu[i + 1]) for i in range(len(cu) - 1) if cu[i + 1] > cu[i]]
+
+    def quantize():
+        ring = oracle.scales.AmaxRing()
+        codes, ds, _ = oracle.pipeline.quantize_step(qb, kb, vb, w.mode, ring=ring, static_values=static_values)
+        return [oracle.quant.dequantize(c, dd) for c, dd in zip(codes, ds)]
+
+    def attend(deq, rows):
+        res = []
+        for s0, s1 in segs:
+            n = min(rows, s1 - s0)
+            for h in range(H):
+                res.append((s0, s1, n, h, oracle.attention._segment_head(
+                    deq[0][s0:s0 + n, h], deq[1][s0:s1, h], deq[2][s0:s1, h], sigma)))
+        return res
+
     t0 = time.perf_counter()
-    codes, ds, _ = oracle.pipeline.quantize_step(qb, kb, vb, w.mode, ring=ring, static_values=static_values)
+    deq = quantize()
     t_quant = time.perf_counter() - t0
-    deq = [oracle.quant.dequantize(c, d) for c, d in zip(codes, ds)]
-    cu = w.cu_seqlens
+    s0, s1 = segs[0]
     t0 = time.perf_counter()
-    done_rows, total_rows = 0, 0
-    for i in range(len(cu) - 1):
-        s0, s1 = int(cu[i]), int(cu[i + 1])
-        n = min(rows_per_head, s1 - s0)
-        total_rows += s1 - s0
-        done_rows += n
-        for h in range(qb.shape[1]):
-            oracle.attention._segment_head(deq[0][s0:s0 + n, h], deq[1][s0:s1, h], deq[2][s0:s1, h],
-                                           np.float64(oracle.attention.default_softmax_scale(qb.shape[2])))
-    t_attn = time.perf_counter() - t0
-    frac = done_rows / max(total_rows, 1)
-    step_s = t_quant + t_attn / frac
-    return {"value": w.flops / step_s / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"quantization of all {3 * qb.size} elements + fp64 attention for {done_rows} of "
-                      f"{total_rows} query rows x {qb.shape[1]} heads (all keys); step time extrapolated "
-                      f"linearly in query rows; measured {t_quant + t_attn:.1f} s of CPU work",
-            "seconds_per_step_est": step_s}
+    oracle.attention._segment_head(deq[0][s0:s0 + min(64, s1 - s0), 0], deq[1][s0:s1, 0], deq[2][s0:s1, 0], sigma)
+    pilot = time.perf_counter() - t0
+    rate = 4.0 * d * min(64, s1 - s0) * (s1 - s0) / max(pilot, 1e-9)      # flop/s of the oracle attention
+    est_step = t_quant + w.flops / rate
+    work_s = t_quant + pilot
+    if est_step <= 30.0:
+        reps = max(1, int(target_s // est_step))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            deq = quantize()
+            rows_out = attend(deq, 1 << 30)
+        elapsed = time.perf_counter() - t0
+        work_s += elapsed
+        value = reps * w.flops / elapsed / 1e12
+        sample = (f"{reps} whole step(s): oracle quantization of all {3 * qb.size} elements + fp64 attention "
+                  f"over every query row of every segment and head; {work_s:.1f} s of CPU work")
+        step_s = elapsed / reps
+    else:
+        frac = max(1e-4, (target_s - t_quant) * rate / w.flops)
+        rows = max(1, int(frac * max(s1 - s0 for s0, s1 in segs)))
+        t0 = time.perf_counter()
+        rows_out = attend(deq, rows)
+        t_attn = time.perf_counter() - t0
+        work_s += t_attn
+        done = sum(4.0 * d * n * (b - a) for a, b, n, _, _ in rows_out)     # flops of the sampled rows
+        step_s = t_quant + t_attn * w.flops / done
+        value = w.flops / step_s / 1e12
+        sample = (f"oracle quantization of all {3 * qb.size} elements + fp64 attention for the first {rows} query "
+                  f"rows of every segment and head (all keys); step time extrapolated linearly in query rows; "
+                  f"{work_s:.1f} s of CPU work")
+    if not compare:
+        return {"value": value, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle", "sample": sample,
+                "seconds_per_step": round(step_s, 3)}
+    vmax = float(np.abs(oracle.quant.bf16_to_f32(vb)).max())
+    err = max(float(np.abs(out_gpu[a:a + n, h].astype(np.float64) - o).max()) for a, _, n, h, o in rows_out)
+    return {"value": value, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle", "sample": sample,
+            "seconds_per_step": round(step_s, 3),
+            "gpu_vs_oracle_max_abs_over_vmax": err / vmax if vmax > 0 else 0.0,
+            "gpu_rows_checked": int(sum(n for _, _, n, _, _ in rows_out))}
+
+
+def attn_traffic(workload, head_dim):
+    """HBM bytes per attention launch from the committed counter summary
+    profiles/traffic_attn_<workload>.md, or None when the summary is missing or
+    was taken on a different attention kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_attn_{workload}.md")
+    src = os.path.join(ROOT, "fp8_quantized_varlen_amd", "csrc", "attn.hip")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        m = re.match(r"^- ([a-z0-9_ ]+): `?([0-9a-f.]+)`?\s*$", line.strip())
+        if m:
+            fields[m.group(1)] = m.group(2)
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("attention kernel source sha256") != sha or "traffic bytes per launch" not in fields:
+        return None
+    return int(float(fields["traffic bytes per launch"]))
 
 
 def main():
@@ -136,7 +200,10 @@ def main():
     st = fv.new_state(dev)
     static_values = None
     if w.mode == "static":
-        static_values = calibrate_static(fv, w, dev)
+        if args.static_values:
+            static_values = [float(x) for x in args.static_values.split(",")]
+        else:
+            static_values = calibrate_static(fv, w, dev)
         fv.state_set_static(st, static_values)
     base = [to_dev(x, dev) for x in (qb, kb, vb)]
     if w.mode == "dynamic":
@@ -212,13 +279,21 @@ def main():
                     "quantize_GBps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
                     "attention_TFLOPs": round(attn_tflops, 2)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": FP8_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4),
+                     "traffic": attn_traffic(w.name, d),
                      "kernel": "attn_kernel<%d>" % d},
         "descale_used": state["descale_used"],
         "wall_s_timed_region": round(t_wall, 3),
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, qb, kb, vb, static_values, args.cpu_rows)
+        # one more step on the unrotated input, so the oracle rows can be compared with it
+        step(0)
+        torch.cuda.synchronize()
+        out_np = out.float().cpu().numpy()
+        # dynamic mode: the GPU ring holds only this input's amax (the scales the oracle's
+        # fresh ring gives) once 16 forwards of it have been pushed
+        same_scales = w.mode == "static" or args.warmup + args.steps >= 16
+        res["cpu_baseline"] = cpu_baseline(w, qb, kb, vb, static_values, out_np, args.cpu_seconds, same_scales)
     print(json.dumps(res), flush=True)
 
 
