@@ -96,6 +96,9 @@ fp8vit_status fp8vit_attn_varlen(const void* q8, const void* k8, const void* v8,
   const int64_t by_max = (int64_t)num_segments * (((int64_t)max_seqlen + bm - 1) / bm);
   const int64_t ntiles = by_total < by_max ? by_total : by_max;
   if (ntiles * num_heads >= ((int64_t)1 << 31)) return FP8VIT_ERR_UNSUPPORTED;
+  // The kernel's buffer descriptors address each e4m3 tensor with 31-bit
+  // offsets, including up to three tiles read past the end of a segment.
+  if (((int64_t)total_tokens + 384) * row >= ((int64_t)1 << 31)) return FP8VIT_ERR_UNSUPPORTED;
   fp8vit::AttnArgs a;
   a.q8 = static_cast<const uint8_t*>(q8);
   a.k8 = static_cast<const uint8_t*>(k8);
@@ -104,6 +107,7 @@ fp8vit_status fp8vit_attn_varlen(const void* q8, const void* k8, const void* v8,
   a.nseg = num_segments;
   a.H = num_heads;
   a.ntiles_ub = (int32_t)ntiles;
+  a.tensor_bytes = (uint32_t)((int64_t)total_tokens * row);
   a.st = static_cast<const DevState*>(d_state);
   a.out = static_cast<uint16_t*>(out);
   a.ld_out = ld_out;

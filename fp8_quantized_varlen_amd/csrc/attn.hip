@@ -7,27 +7,27 @@
 // with Q8/K8/V8 the e4m3 codes and dq/dk/dv the per-tensor descales.
 //
 // Design (MI355X-first, not a port of any kernel on the pages):
-//  * A workgroup owns 128 queries of one (segment, head): WAVES waves of
-//    QB 16-query MFMA column blocks each (8x1 or 4x2).
-//  * K/V tiles of 128 keys are double-buffered in LDS. The next tile's global
-//    loads are issued into registers when a tile starts and stored into the
-//    other buffer halfway through it: one barrier per tile, global latency
-//    hidden behind the MFMA/softmax work.
+//  * A workgroup owns BM = 16*QB*WAVES queries of one (segment, head); each
+//    wave owns 16*QB of them and runs over every key of the segment.
+//  * K/V tiles of 128 keys go global -> LDS by the buffer-load LDS DMA
+//    (buffer_load_dwordx4 ... lds): no staging registers, no LDS store
+//    instructions, issued a whole iteration before the tile is needed and
+//    bounds-checked by the buffer descriptor (reads past the tensor give 0).
 //  * S^T = K Q^T on v_mfma_f32_16x16x128_f8f6f4 (K rows as the A operand, Q as
 //    B), d zero-padded to 128 for head_dim 72. A rows are permuted so that lane
 //    group g holds keys 32g..32g+31 of its query: the fp32 S^T registers turn
-//    in place into the B operand of the next product (no LDS round trip).
+//    in place into the B operand of the P.V product (no LDS round trip).
 //  * O^T = V^T P^T on the same MFMA; V^T comes from row-major V in LDS through
-//    ds_read_b64_tr_b8 (byte transpose on read). Column 72 of the hd72 V tile
-//    holds 1.0, so the same MFMAs accumulate the row sum of the probabilities
-//    actually used; hd128 appends a constant ones block.
-//  * One-pass online softmax in exp2 units with a lazy reference max m_ref:
-//    P~ = 2^7 * exp2(t - m_ref) is formed right after each 16-key S^T block
-//    while a per-lane running max is kept; S^T of the next block is already on
-//    the matrix core. Only if some score of the tile exceeds m_ref + 1.75
-//    (then P~ could pass 448, e4m3's largest value) is the row max reduced
-//    across lanes, O rescaled and the tile's probabilities recomputed. The
-//    first tile always takes that path (m_ref = -inf).
+//    ds_read_b64_tr_b8 (byte transpose on read). The A operand row of column
+//    72 (hd72) is replaced by 1.0 in registers, and hd128 appends a constant
+//    ones block, so the same MFMAs accumulate the row sum of the
+//    probabilities actually used.
+//  * Software pipeline over key tiles: iteration j holds the whole S(j) tile
+//    in registers, so its maximum is known before any probability is formed;
+//    S(j+1) and the previous tile's P(j-1).V(j-1) run on the matrix core while
+//    the VALU forms P(j). Lazy reference max m_ref: P~ = 2^7 * exp2(t - m_ref)
+//    and m_ref moves only when a score exceeds m_ref + 1.75 (P~ could then pass
+//    448, e4m3's largest value); O is rescaled at the end of that iteration.
 //  * P~ goes to the FP8 MFMA as two e4m3 terms, hi = e4m3(P~) and
 //    lo = e4m3(P~ - hi): a single e4m3 term adds ~2.5% relative error to O.
 //  * Work items are (head, query tile); consecutive items of one head are
@@ -42,55 +42,46 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 typedef __attribute__((address_space(3))) v4i lds_v4i;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBN = 128;             // keys per tile
 constexpr float kExpBias = 7.0f;     // P~ = 2^7 * exp2(t - m_ref)
 constexpr float kLazy = 1.75f;       // log2 growth of the max tolerated before rescaling
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
 
 template <int D> struct Cfg;
-// KS/VS: LDS row strides in bytes. NCB: 16-column blocks of O^T including the
-// ones column. CHB x ROWCH: bytes per global load x loads per K/V row.
+// KS/VS: LDS row strides in bytes (multiples of 16: the DMA moves 16-byte
+// chunks, so a row holds the head's D bytes followed by the first bytes of
+// the next head; those only ever meet zero Q bytes or discarded O columns).
+// NCB: 16-column blocks of O^T including the ones column.
 // WAVES x QB x 16 = BM queries per workgroup.
-// hd72: K rows are 80 bytes (72 + 8 zero bytes); the d-padding lanes of the
-// S^T operand read past their row into the next one, which only meets the
-// zero bytes of the Q operand, or read a 32-byte zero block after the tile.
 template <> struct Cfg<72> {
-  static constexpr int KS = 80, VS = 80, NCB = 5, CHB = 8, ROWCH = 9, ONES_CB = 4, ONES_LANE0 = 32;
+  static constexpr int KS = 80, VS = 80, NCB = 5, ONES_CB = 4, ONES_LANE0 = 32;
   static constexpr int WAVES = 4, QB = 1, MIN_WAVES_PER_EU = 3, BM = 64;
 };
 template <> struct Cfg<128> {
-  static constexpr int KS = 144, VS = 144, NCB = 9, CHB = 16, ROWCH = 8, ONES_CB = 8, ONES_LANE0 = 0;
+  static constexpr int KS = 144, VS = 144, NCB = 9, ONES_CB = 8, ONES_LANE0 = 0;
   static constexpr int WAVES = 8, QB = 1, MIN_WAVES_PER_EU = 2, BM = 128;
 };
 
 // LDS placement of a tile's rows.
 //  K: key k sits in row 4*(k%32) + k/32, so the 16 keys of one S^T block
-//     (32a + 4t + b, a, b = 0..3) occupy 16 consecutive rows 16t..16t+15,
-//     whose 16-byte pieces fall on distinct banks.
-//  V: key k sits at byte k*VS + 64*(k/32); the 64-byte gap between 32-key
-//     groups spreads the four lane groups of a transpose read over the banks.
-__device__ __forceinline__ int k_row(int key) { return 4 * (key & 31) + (key >> 5); }
-template <int D> __device__ __forceinline__ int v_off(int key) { return key * Cfg<D>::VS + 64 * (key >> 5); }
+//     (32a + 4t + b, a, b = 0..3) occupy 16 consecutive rows 16t..16t+15.
+//  V: key k sits in row k.
+__device__ __forceinline__ int k_key(int row) { return 32 * (row & 3) + (row >> 2); }
 
 template <int D> struct Stage {
   static constexpr int THREADS = 64 * Cfg<D>::WAVES;
-  // Staging: TPR threads per K/V row, each moving CPT chunks starting at
-  // chunk P0_STEP * (tid % TPR) (neighbours may overlap by a chunk; both then
-  // store the same bytes).
-  static constexpr int TPR = THREADS / kBN;
-  static constexpr int CPT = (Cfg<D>::ROWCH + TPR - 1) / TPR;
-  static constexpr int P0_STEP = TPR > 1 ? (Cfg<D>::ROWCH - CPT) / (TPR - 1) : 0;
-  static_assert(TPR >= 1 && THREADS % kBN == 0, "staging shape");
-  static_assert(P0_STEP * (TPR - 1) + CPT == Cfg<D>::ROWCH && P0_STEP <= CPT, "staging covers each row");
-  static constexpr int KZERO = kBN * Cfg<D>::KS;                       // 32 bytes after the rows
-  static constexpr int KBUF = KZERO + 32, VBUF = kBN * Cfg<D>::VS + 64 * (kBN / 32 - 1);
-  using chunk_t = typename std::conditional<Cfg<D>::CHB == 8, u32x2, u32x4>::type;
+  static constexpr int KZERO = kBN * Cfg<D>::KS;                 // 32 zero bytes after the K rows
+  static constexpr int KBUF = KZERO + 32, VBUF = kBN * Cfg<D>::VS;
+  // DMA: one wave instruction moves 64 chunks of 16 bytes (1 KB) of a tile.
+  static constexpr int NI = kBN * Cfg<D>::KS / 1024;              // instructions per K (or V) tile
+  static constexpr int NIW = (2 * NI + Cfg<D>::WAVES - 1) / Cfg<D>::WAVES;   // per wave, K and V together
+  static_assert(kBN * Cfg<D>::KS % 1024 == 0 && Cfg<D>::KS == Cfg<D>::VS, "DMA tiling");
 };
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
@@ -102,40 +93,14 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Global -> register prefetch of this thread's chunks of one K/V row of a
-// tile. Rows past the segment end read the last valid row: those keys are
-// masked or multiplied by P = 0. kg/vg point at this thread's first chunk of
-// key 0 of the segment for this head.
-template <int D>
-__device__ __forceinline__ void prefetch_row(const uint8_t* kg, const uint8_t* vg, uint32_t row_stride, int key,
-                                             typename Stage<D>::chunk_t* kr, typename Stage<D>::chunk_t* vr) {
-  using S = Stage<D>;
-  const uint32_t off = (uint32_t)key * row_stride;
-#pragma unroll
-  for (int i = 0; i < S::CPT; ++i) {
-    kr[i] = *reinterpret_cast<const typename S::chunk_t*>(kg + off + Cfg<D>::CHB * i);
-    vr[i] = *reinterpret_cast<const typename S::chunk_t*>(vg + off + Cfg<D>::CHB * i);
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void commit_row(uint8_t* kdst, uint8_t* vdst, const typename Stage<D>::chunk_t* kr,
-                                           const typename Stage<D>::chunk_t* vr) {
-  using S = Stage<D>;
-#pragma unroll
-  for (int i = 0; i < S::CPT; ++i) {
-    *reinterpret_cast<typename S::chunk_t*>(kdst + Cfg<D>::CHB * i) = kr[i];
-    *reinterpret_cast<typename S::chunk_t*>(vdst + Cfg<D>::CHB * i) = vr[i];
-  }
-}
-
 // A operand of S^T block t: lane row i16 <-> key 32*(i16/4) + 4t + i16%4, d bytes
 // 32g..32g+31. `kl` is the lane's byte offset for t = 0 (k_lane_offset); block t
 // adds 16 rows. hd72: lane groups 2 and 3 read bytes 64..95 (8 data bytes, then
-// bytes that only meet zero bytes of the Q operand).
+// bytes that only meet zero bytes of the Q operand; row 127 runs into the zero
+// bytes after the tile).
 template <int D>
 __device__ __forceinline__ int k_lane_offset(int g, int i16) {
-  const int krow = 4 * (i16 & 3) + (i16 >> 2);            // = k_row(32*(i16/4) + i16%4)
+  const int krow = 4 * (i16 & 3) + (i16 >> 2);            // row of key 32*(i16/4) + i16%4
   return krow * Cfg<D>::KS + (D == 72 ? min(32 * g, 64) : 32 * g);
 }
 template <int D>
@@ -151,7 +116,7 @@ __device__ __forceinline__ v8i k_operand(const lds_u8* kl, int t) {
 // byte offset (v_lane_offset); the 8-key steps and the column block are constants.
 template <int D>
 __device__ __forceinline__ int v_lane_offset(int g, int i16) {
-  return v_off<D>(32 * g + (i16 >> 1)) + 8 * (i16 & 1);
+  return (32 * g + (i16 >> 1)) * Cfg<D>::VS + 8 * (i16 & 1);
 }
 template <int D>
 __device__ __forceinline__ v8i v_operand(const lds_u8* vl, int cb) {
@@ -173,13 +138,36 @@ __device__ __forceinline__ int2 probs_to_fp8(const v4f& s, float c, float nb) {
   const float p1 = __builtin_amdgcn_exp2f(fmaf(s[1], c, nb));
   const float p2 = __builtin_amdgcn_exp2f(fmaf(s[2], c, nb));
   const float p3 = __builtin_amdgcn_exp2f(fmaf(s[3], c, nb));
-  int h = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+  // The first conversion of each pair leaves the upper half of its "old"
+  // operand, which the second one overwrites: any dead register will do.
+  int h = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __float_as_int(s[0]), false);
   h = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, h, true);
   const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
   const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
-  int l = __builtin_amdgcn_cvt_pk_fp8_f32(p0 - h01[0], p1 - h01[1], 0, false);
+  int l = __builtin_amdgcn_cvt_pk_fp8_f32(p0 - h01[0], p1 - h01[1], __float_as_int(s[1]), false);
   l = __builtin_amdgcn_cvt_pk_fp8_f32(p2 - h23[0], p3 - h23[1], l, true);
   return make_int2(h, l);
+}
+
+// This wave's share of the DMA of one K tile (koff: its global byte offset)
+// into kdst and, with_v, one V tile into vdst. Instruction i = wave + WAVES*n
+// of a tile moves chunks 64*i .. 64*i+63 of K (i < NI) or of V (NI <= i < 2 NI);
+// dma_off[n] holds the lane's global offset for tile 0.
+template <int D>
+__device__ __forceinline__ void dma_issue(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                          const uint32_t* dma_off, int wave, uint32_t koff, uint8_t* kdst,
+                                          uint32_t voff, uint8_t* vdst, bool with_v) {
+  using S = Stage<D>;
+#pragma unroll
+  for (int n = 0; n < S::NIW; ++n) {
+    const int i = wave + Cfg<D>::WAVES * n;   // wave-uniform
+    if (i < S::NI) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kdst + 1024 * i), 16, dma_off[n] + koff, 0, 0, 0);
+    } else if (i < 2 * S::NI && with_v) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vdst + 1024 * (i - S::NI)), 16, dma_off[n] + voff, 0,
+                                               0, 0);
+    }
+  }
 }
 
 template <int D>
@@ -191,8 +179,13 @@ void attn_kernel(AttnArgs a) {
   constexpr int BMW = 16 * QB;
   constexpr int kBM = C::BM;
   static_assert(C::WAVES * BMW == kBM, "block shape");
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[2 * S::KBUF];
-  __shared__ __attribute__((aligned(16))) uint8_t v_lds[3 * S::VBUF];
+  // Two K and two V buffers, as separate objects: the compiler can then tell
+  // the DMA's target apart from the buffer being read and does not wait for
+  // the DMA before each LDS read.
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[S::KBUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[S::KBUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[S::VBUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[S::VBUF];
 
   // ---- work item: XCD-grouped (head, query tile) -> segment by prefix scan ----
   const int G = gridDim.x;
@@ -212,36 +205,46 @@ void attn_kernel(AttnArgs a) {
   const int ntiles = (L + kBN - 1) / kBN;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, i16 = lane & 15;
 
-  // ---- staging geometry; first K/V tile in flight while the constants are written ----
-  const int srow = tid / S::TPR;
-  const int schunk = S::P0_STEP * (tid % S::TPR);
+  // ---- DMA geometry ----
+  // Buffer descriptors start at key 0 of the segment for this head; their
+  // record count ends at the end of the tensor, so chunks past it read 0.
   const uint32_t row_stride = (uint32_t)a.H * D;
-  const int64_t seg_off = ((int64_t)s0 * a.H + h) * D + Cfg<D>::CHB * schunk;
-  const uint8_t* kg = a.k8 + seg_off;
-  const uint8_t* vg = a.v8 + seg_off;
-  const int k_stage = k_row(srow) * C::KS + Cfg<D>::CHB * schunk;   // LDS offsets within a buffer
-  const int v_stage = v_off<D>(srow) + Cfg<D>::CHB * schunk;
-  typename S::chunk_t kr[S::CPT], vr[S::CPT];
-  prefetch_row<D>(kg, vg, row_stride, min(srow, L - 1), kr, vr);
-  for (int r = tid; r < 2 * (kBN + 4); r += S::THREADS) {
-    uint8_t* kr0 = k_lds + (r / (kBN + 4)) * S::KBUF;
-    const int rr = r % (kBN + 4);
-    if (rr < kBN) {
+  const uint32_t seg_off = ((uint32_t)s0 * (uint32_t)a.H + (uint32_t)h) * D;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.k8 + seg_off), (short)0, (int)(a.tensor_bytes - seg_off), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.v8 + seg_off), (short)0, (int)(a.tensor_bytes - seg_off), kRsrcWord3);
+  // This wave's DMA instructions n = 0..NIW-1 are instruction i = wave + WAVES*n
+  // of the tile (K for i < NI, V after). Lane l of instruction ii moves the
+  // 16-byte chunk c = 64*ii + l of the tile's LDS image: row c / (KS/16),
+  // piece c % (KS/16). dma_off: its byte offset in global memory for tile 0.
+  uint32_t dma_off[S::NIW];
 #pragma unroll
-      for (int b = D; b < C::KS; b += 8) *reinterpret_cast<uint2*>(kr0 + rr * C::KS + b) = make_uint2(0u, 0u);
-    } else {
-      *reinterpret_cast<uint2*>(kr0 + S::KZERO + 8 * (rr - kBN)) = make_uint2(0u, 0u);
-    }
+  for (int n = 0; n < S::NIW; ++n) {
+    const int i = wave + C::WAVES * n;
+    const int ii = i < S::NI ? i : i - S::NI;
+    const int c = 64 * ii + lane;
+    const int row = c / (C::KS / 16), piece = c % (C::KS / 16);
+    const int key = i < S::NI ? k_key(row) : row;
+    dma_off[n] = (uint32_t)key * row_stride + 16u * (uint32_t)piece;
   }
-  for (int r = tid; r < 3 * kBN; r += S::THREADS) {
-    uint8_t* vr0 = v_lds + (r / kBN) * S::VBUF + v_off<D>(r % kBN);
-#pragma unroll
-    for (int b = 0; b < C::VS; b += 8)
-      *reinterpret_cast<uint2*>(vr0 + b) = make_uint2((D == 72 && b == 72) ? 0x38u : 0u, 0u);
-  }
+  // Issue this wave's DMA of K tile tk into kdst and (with_v) V tile tv into vdst.
+  auto dma_tiles = [&](int tk, uint8_t* kdst, int tv, uint8_t* vdst, bool with_v) {
+    dma_issue<D>(krs, vrs, dma_off, wave, (uint32_t)tk * kBN * row_stride, kdst, (uint32_t)tv * kBN * row_stride,
+                 vdst, with_v);
+  };
+
+  dma_tiles(0, k_lds0, 0, v_lds0, false);   // K(0)
+  dma_tiles(1, k_lds1, 0, v_lds0, false);   // K(1)
+  // Zero the 32 bytes after each K tile (read only against zero Q bytes) and
+  // V buffer 1: V(-1) meets P = 0 in the first iteration.
+  for (int r = tid; r < 2 * 4; r += S::THREADS)
+    *reinterpret_cast<uint2*>((r < 4 ? k_lds0 : k_lds1) + S::KZERO + 8 * (r % 4)) = make_uint2(0u, 0u);
+  for (int r = tid; r < S::VBUF / 16; r += S::THREADS)
+    *reinterpret_cast<uint4*>(v_lds1 + 16 * r) = make_uint4(0u, 0u, 0u, 0u);
 
   const float dq = a.st->descale_used[0], dk = a.st->descale_used[1], dv = a.st->descale_used[2];
   const float cexp = a.softmax_scale * dq * dk * kLog2e;   // raw score -> log2 units (> 0)
@@ -285,145 +288,177 @@ void attn_kernel(AttnArgs a) {
   for (int qb = 0; qb < QB; ++qb) mref[qb] = thr[qb] = -INFINITY;
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
 
-  __syncthreads();   // zero fill above overlaps the rows stored next
-  commit_row<D>(k_lds + k_stage, v_lds + v_stage, kr, vr);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's DMA of K(0), K(1)
   __syncthreads();
   const int kl_lane = k_lane_offset<D>(g, i16);
   const int vl_lane = v_lane_offset<D>(g, i16);
 
-  // P of the previous tile: its O^T += V^T P^T products are interleaved with
-  // the softmax VALU work of the current tile (matrix core and VALU overlap
-  // inside each wave). V is triple-buffered so that the previous tile's V
-  // stays in LDS while the next one is being stored. Before the first tile the
-  // "previous" P is zero and its V buffer holds zeros, so the products add 0.
-  v8i phi_prev[QB], plo_prev[QB];
+  // Software pipeline over key tiles. Iteration j holds S(j) in registers
+  // (computed during iteration j-1), so the tile's maximum is known before
+  // any probability is formed. Its S(j+1) = K(j+1) Q^T products and the
+  // O^T += V(j-1)^T P(j-1)^T products of the previous tile are interleaved
+  // with the softmax VALU work on S(j). LDS: K(j+1) and V(j-1) are read while
+  // the DMA fills the other buffer of each pair with K(j+2) and V(j); one
+  // barrier per iteration.
+  struct PSet { v8i hi[QB], lo[QB]; };
+  PSet pa, pb;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) phi_prev[qb] = plo_prev[qb] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-  const v8i ones_op = (i16 == 0) ? v8i{0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                                       0x38383838, 0x38383838}
+  for (int qb = 0; qb < QB; ++qb) pb.hi[qb] = pb.lo[qb] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  constexpr int kOne8 = 0x38383838;   // four e4m3 1.0
+  // hd128: constant A operand of the ones block (row 0 = 1.0); hd72: the A
+  // operand row of column 72 (lanes with i16 == 8 of block 4) is set to 1.0.
+  const v8i ones_op = (i16 == 0) ? v8i{kOne8, kOne8, kOne8, kOne8, kOne8, kOne8, kOne8, kOne8}
                                  : v8i{0, 0, 0, 0, 0, 0, 0, 0};
-  auto pv_block = [&](const lds_u8* vbp, int cb) {
-    const v8i vop = (D == 128 && cb == 8) ? ones_op : v_operand<D>(vbp, cb);
+  const bool ones_row = (D == 72) && (i16 == 8);
+  auto v_op = [&](const lds_u8* vbp, int cb) -> v8i {
+    if (D == 128 && cb == 8) return ones_op;
+    v8i r = v_operand<D>(vbp, cb);
+    if (D == 72 && cb == C::ONES_CB) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r[e] = ones_row ? kOne8 : r[e];
+    }
+    return r;
+  };
+  auto pv_block = [&](const PSet& pp, const v8i& vop, int cb) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      o[qb][cb] = mfma_fp8(vop, phi_prev[qb], o[qb][cb]);
-      o[qb][cb] = mfma_fp8(vop, plo_prev[qb], o[qb][cb]);
+      o[qb][cb] = mfma_fp8(vop, pp.hi[qb], o[qb][cb]);
+      o[qb][cb] = mfma_fp8(vop, pp.lo[qb], o[qb][cb]);
     }
   };
 
-  // One pass over the 8 S^T blocks of a tile. Template flags keep the
-  // unrolled body free of branches: PARTIAL masks keys past the segment end
-  // (last tile only), WITH_PV interleaves the previous tile's P.V, COMMIT
-  // stores the prefetched next tile after block 3.
-  v8i phi[QB], plo[QB];
-  float lm[QB];
-  auto run_pass = [&](auto partial_c, auto pv_c, auto commit_c, int j) {
-    constexpr bool PARTIAL = decltype(partial_c)::value;
-    constexpr bool WITH_PV = decltype(pv_c)::value;
-    constexpr bool COMMIT = decltype(commit_c)::value;
-    const int kv0 = j * kBN;
-    // One base register per operand and tile; the per-block steps become
-    // immediate offsets of the LDS reads (the empty asm keeps the compiler
-    // from hoisting one precomputed address per read out of the loop).
-    uint32_t kbase = (uint32_t)((j & 1) * S::KBUF + kl_lane);
-    uint32_t vbase = (uint32_t)(((j + 2) % 3) * S::VBUF + vl_lane);
-    asm volatile("" : "+v"(kbase), "+v"(vbase));
-    const lds_u8* kl = (const lds_u8*)k_lds + kbase;
-    const lds_u8* vprev = (const lds_u8*)v_lds + vbase;   // V of tile j-1
-    float nb[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      nb[qb] = kExpBias - mref[qb];
-      lm[qb] = -INFINITY;
-    }
-    v8i kop = k_operand<D>(kl, 0);
-    v4f sa[QB], sb[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) sa[qb] = mfma_fp8(kop, qop[qb], zero4);
-    kop = k_operand<D>(kl, 1);
+  // S(0)
+  v4f sc[QB][8];
+  {
+    uint32_t kbase = (uint32_t)kl_lane;
+    asm volatile("" : "+v"(kbase));
+    const lds_u8* kl = (const lds_u8*)k_lds0 + kbase;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      if (t + 1 < 8) {
+      const v8i kop = k_operand<D>(kl, t);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sb[qb] = mfma_fp8(kop, qop[qb], zero4);
-        if (t + 2 < 8) kop = k_operand<D>(kl, t + 2);
-      }
-      if (WITH_PV) {                     // one 16-column block per 16-key block
-        if (t < C::NCB) pv_block(vprev, t);
-        if (t == 7 && C::NCB > 8) pv_block(vprev, 8);
-      }
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        if (PARTIAL) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sa[qb][r] = (kv0 + 32 * g + 4 * t + r >= L) ? -INFINITY : sa[qb][r];
-        }
-        lm[qb] = fmaxf(fmaxf(fmaxf(fmaxf(lm[qb], sa[qb][0]), sa[qb][1]), sa[qb][2]), sa[qb][3]);
-        const int2 p = probs_to_fp8(sa[qb], cexp, nb[qb]);
-        phi[qb][t] = p.x;
-        plo[qb][t] = p.y;
-        if (t + 1 < 8) sa[qb] = sb[qb];
-      }
-      // The buffers of the next tile are free since the last barrier: store
-      // it early so its registers do not stay live through the pass.
-      if (COMMIT && t == 3)
-        commit_row<D>(k_lds + ((j + 1) & 1) * S::KBUF + k_stage, v_lds + ((j + 1) % 3) * S::VBUF + v_stage, kr, vr);
+      for (int qb = 0; qb < QB; ++qb) sc[qb][t] = mfma_fp8(kop, qop[qb], zero4);
     }
-  };
-  // Overflow check after a pass: a score above its row's threshold means P~
-  // may exceed 448. Then reduce the row max over the four lane groups, move
-  // the reference max, rescale O (which holds every earlier tile by now) and
-  // recompute this tile's probabilities.
-  auto need_redo = [&]() {
-    // Keep the pass' probabilities computed here, interleaved with its MFMAs,
-    // rather than sunk past the branch into the common path.
+  }
+  __syncthreads();   // K buffer 0 receives K(2) in iteration 0
+
+  // One iteration; LAST: keys of S(j) past the segment end are masked and
+  // there is no S(j+1). ODD = j & 1 selects the buffers.
+  auto iteration = [&](auto last_c, auto odd_c, int j, PSet& cur, const PSet& prev) {
+    constexpr bool LAST = decltype(last_c)::value;
+    constexpr bool ODD = decltype(odd_c)::value;
+    uint8_t* const k_fill = ODD ? k_lds1 : k_lds0;     // K(j+2)
+    uint8_t* const v_fill = ODD ? v_lds1 : v_lds0;     // V(j)
+    const uint8_t* const k_read = ODD ? k_lds0 : k_lds1;   // K(j+1)
+    const uint8_t* const v_read = ODD ? v_lds0 : v_lds1;   // V(j-1)
+    dma_tiles(j + 2, k_fill, j, v_fill, true);
+    if (LAST) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) asm volatile("" : "+v"(phi[qb]), "+v"(plo[qb]));
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            sc[qb][t][r] = (j * kBN + 32 * g + 4 * t + r >= L) ? -INFINITY : sc[qb][t][r];
+    }
+    // Lazy reference max: only when a score exceeds its row's threshold is the
+    // row max reduced across the four lane groups and m_ref moved. O is
+    // rescaled at the end of the iteration, after the previous tile's
+    // products (formed with the old m_ref) have been added.
+    float lm[QB];
     bool over = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) over = over || (lm[qb] > thr[qb]);
-    if (__ballot(over) == 0ull) return false;
-#pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float m = lm[qb];
-      m = fmaxf(m, __shfl_xor(m, 16, 64));
-      m = fmaxf(m, __shfl_xor(m, 32, 64));
-      const float mn = fmaxf(mref[qb], m * cexp);
-      const float alpha = __builtin_amdgcn_exp2f(mref[qb] - mn);
-      mref[qb] = mn;
-      thr[qb] = (mn + kLazy) / cexp;
+      float m = -INFINITY;
 #pragma unroll
-      for (int cb = 0; cb < C::NCB; ++cb) o[qb][cb] *= alpha;
+      for (int t = 0; t < 8; ++t)
+        m = fmaxf(fmaxf(fmaxf(fmaxf(m, sc[qb][t][0]), sc[qb][t][1]), sc[qb][t][2]), sc[qb][t][3]);
+      lm[qb] = m;
+      over = over || (m > thr[qb]);
     }
-    return true;
+    const bool rescale = __ballot(over) != 0ull;
+    float alpha[QB];
+    if (rescale) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float m = lm[qb];
+        m = fmaxf(m, __shfl_xor(m, 16, 64));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        const float mn = fmaxf(mref[qb], m * cexp);
+        alpha[qb] = __builtin_amdgcn_exp2f(mref[qb] - mn);
+        mref[qb] = mn;
+        thr[qb] = (mn + kLazy) / cexp;
+      }
+    }
+    float nb[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) nb[qb] = kExpBias - mref[qb];
+
+    uint32_t kbase = (uint32_t)kl_lane, vbase = (uint32_t)vl_lane;
+    asm volatile("" : "+v"(kbase), "+v"(vbase));
+    const lds_u8* kl = (const lds_u8*)k_read + kbase;
+    const lds_u8* vprev = (const lds_u8*)v_read + vbase;
+    // Operands are read one step ahead of their products; the scheduling
+    // barrier at the end of each step keeps the compiler from hoisting every
+    // LDS read of the iteration to its top (that would cost ~40 VGPRs).
+    v8i kop, vop;
+    if (!LAST) kop = k_operand<D>(kl, 0);
+    vop = v_op(vprev, 0);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (t < C::NCB) {
+        const v8i vcur = vop;
+        if (t + 1 < C::NCB) vop = v_op(vprev, t + 1);
+        pv_block(prev, vcur, t);
+      }
+      if (t == 7 && C::NCB > 8) pv_block(prev, ones_op, 8);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int2 p = probs_to_fp8(sc[qb][t], cexp, nb[qb]);
+        cur.hi[qb][t] = p.x;
+        cur.lo[qb][t] = p.y;
+        // P of this tile is consumed only by the next iteration; pin its
+        // computation here, interleaved with this step's MFMAs, instead of
+        // letting it sink to its use.
+        asm volatile("" : "+v"(cur.hi[qb]), "+v"(cur.lo[qb]));
+      }
+      if (!LAST) {
+        const v8i kcur = kop;
+        if (t + 1 < 8) kop = k_operand<D>(kl, t + 1);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sc[qb][t] = mfma_fp8(kcur, qop[qb], zero4);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (rescale) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int cb = 0; cb < C::NCB; ++cb) o[qb][cb] *= alpha[qb];
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's DMA of K(j+2), V(j)
+    __syncthreads();
   };
-  auto shift_p = [&]() {
+  // P.V of the last tile; its V arrived before the last barrier
+  auto final_pv = [&](const PSet& pp, const uint8_t* vbuf) {
+    const lds_u8* vlast = (const lds_u8*)vbuf + vl_lane;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      phi_prev[qb] = phi[qb];
-      plo_prev[qb] = plo[qb];
-    }
+    for (int cb = 0; cb < C::NCB; ++cb) pv_block(pp, v_op(vlast, cb), cb);
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
-
-  // full tiles
-  for (int j = 0; j + 1 < ntiles; ++j) {
-    prefetch_row<D>(kg, vg, row_stride, min((j + 1) * kBN + srow, L - 1), kr, vr);
-    run_pass(F_{}, T_{}, T_{}, j);
-    if (need_redo()) run_pass(F_{}, F_{}, F_{}, j);
-    shift_p();
-    __syncthreads();
+  int j = 0;
+  for (; j + 2 < ntiles; j += 2) {
+    iteration(F_{}, F_{}, j, pa, pb);
+    iteration(F_{}, T_{}, j + 1, pb, pa);
   }
-  // last tile (keys past the segment end masked), then its own P.V
-  {
-    const int j = ntiles - 1;
-    run_pass(T_{}, T_{}, F_{}, j);
-    if (need_redo()) run_pass(T_{}, F_{}, F_{}, j);
-    shift_p();
-    const lds_u8* vlast = (const lds_u8*)v_lds + (j % 3) * S::VBUF + vl_lane;
-#pragma unroll
-    for (int cb = 0; cb < C::NCB; ++cb) pv_block(vlast, cb);
+  if (j + 1 < ntiles) {
+    iteration(F_{}, F_{}, j, pa, pb);
+    iteration(T_{}, T_{}, j + 1, pb, pa);
+    final_pv(pb, v_lds1);
+  } else {
+    iteration(T_{}, F_{}, j, pa, pb);
+    final_pv(pa, v_lds0);
   }
 
   // ---- epilogue: divide by the row sum (ones column), scale by dv, bf16 ----

@@ -52,6 +52,7 @@ struct AttnArgs {
   int32_t nseg;
   int32_t H;
   int32_t ntiles_ub;     // upper bound on query tiles per head
+  uint32_t tensor_bytes; // T * H * d: bytes of each of q8, k8, v8
   const DevState* st;
   uint16_t* out;
   int64_t ld_out;

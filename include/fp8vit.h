@@ -146,7 +146,9 @@ fp8vit_status fp8vit_quantize_qkv(const void* q, const void* k, const void* v,
  * O = softmax(Q^ K^T * scale) V^ per segment and head, where Q^ K^ V^ are the
  * dequantized e4m3 tensors; products on FP8 MFMA with fp32 accumulation; the
  * probabilities are carried to the P.V product in two e4m3 terms.
- * Errors: ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_HIP. */
+ * Errors: ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED (also when
+ * (total_tokens + 384) * H * d reaches 2^31: the kernel addresses each e4m3
+ * tensor with 31-bit offsets), ERR_HIP. */
 fp8vit_status fp8vit_attn_varlen(const void* q8, const void* k8, const void* v8,
                                  const int32_t* d_cu_seqlens, int32_t num_segments,
                                  int32_t max_seqlen, int32_t total_tokens, int32_t num_heads,
