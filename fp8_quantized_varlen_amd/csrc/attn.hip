@@ -61,7 +61,7 @@ template <int D> struct Cfg;
 // WAVES x QB x 16 = BM queries per workgroup.
 template <> struct Cfg<72> {
   static constexpr int KS = 80, VS = 80, NCB = 5, ONES_CB = 4, ONES_LANE0 = 32;
-  static constexpr int WAVES = 4, QB = 1, MIN_WAVES_PER_EU = 3, BM = 64;
+  static constexpr int WAVES = 8, QB = 1, MIN_WAVES_PER_EU = 4, BM = 128;
 };
 template <> struct Cfg<128> {
   static constexpr int KS = 144, VS = 144, NCB = 9, ONES_CB = 8, ONES_LANE0 = 0;
@@ -133,18 +133,19 @@ __device__ __forceinline__ v8i v_operand(const lds_u8* vl, int cb) {
 
 // Two e4m3 terms of four probabilities P~ = exp2(s*c + nb), packed as one
 // dword of the P^T operand (hi) and one of the correction term (lo).
-__device__ __forceinline__ int2 probs_to_fp8(const v4f& s, float c, float nb) {
+// old_hi/old_lo: the dwords being replaced. The first conversion of each pair
+// keeps the upper half of its tied "old" operand (the second one overwrites
+// it), so passing the dead destination dword lets the result land in place.
+__device__ __forceinline__ int2 probs_to_fp8(const v4f& s, float c, float nb, int old_hi, int old_lo) {
   const float p0 = __builtin_amdgcn_exp2f(fmaf(s[0], c, nb));
   const float p1 = __builtin_amdgcn_exp2f(fmaf(s[1], c, nb));
   const float p2 = __builtin_amdgcn_exp2f(fmaf(s[2], c, nb));
   const float p3 = __builtin_amdgcn_exp2f(fmaf(s[3], c, nb));
-  // The first conversion of each pair leaves the upper half of its "old"
-  // operand, which the second one overwrites: any dead register will do.
-  int h = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __float_as_int(s[0]), false);
+  int h = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, old_hi, false);
   h = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, h, true);
   const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
   const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
-  int l = __builtin_amdgcn_cvt_pk_fp8_f32(p0 - h01[0], p1 - h01[1], __float_as_int(s[1]), false);
+  int l = __builtin_amdgcn_cvt_pk_fp8_f32(p0 - h01[0], p1 - h01[1], old_lo, false);
   l = __builtin_amdgcn_cvt_pk_fp8_f32(p2 - h23[0], p3 - h23[1], l, true);
   return make_int2(h, l);
 }
@@ -237,14 +238,11 @@ void attn_kernel(AttnArgs a) {
                  vdst, with_v);
   };
 
-  dma_tiles(0, k_lds0, 0, v_lds0, false);   // K(0)
+  dma_tiles(0, k_lds0, 0, v_lds0, true);    // K(0), V(0)
   dma_tiles(1, k_lds1, 0, v_lds0, false);   // K(1)
-  // Zero the 32 bytes after each K tile (read only against zero Q bytes) and
-  // V buffer 1: V(-1) meets P = 0 in the first iteration.
+  // Zero the 32 bytes after each K tile (read only against zero Q bytes).
   for (int r = tid; r < 2 * 4; r += S::THREADS)
     *reinterpret_cast<uint2*>((r < 4 ? k_lds0 : k_lds1) + S::KZERO + 8 * (r % 4)) = make_uint2(0u, 0u);
-  for (int r = tid; r < S::VBUF / 16; r += S::THREADS)
-    *reinterpret_cast<uint4*>(v_lds1 + 16 * r) = make_uint4(0u, 0u, 0u, 0u);
 
   const float dq = a.st->descale_used[0], dk = a.st->descale_used[1], dv = a.st->descale_used[2];
   const float cexp = a.softmax_scale * dq * dk * kLog2e;   // raw score -> log2 units (> 0)
@@ -288,22 +286,21 @@ void attn_kernel(AttnArgs a) {
   for (int qb = 0; qb < QB; ++qb) mref[qb] = thr[qb] = -INFINITY;
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
 
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's DMA of K(0), K(1)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's DMA of K(0), K(1), V(0)
   __syncthreads();
   const int kl_lane = k_lane_offset<D>(g, i16);
   const int vl_lane = v_lane_offset<D>(g, i16);
 
   // Software pipeline over key tiles. Iteration j holds S(j) in registers
   // (computed during iteration j-1), so the tile's maximum is known before
-  // any probability is formed. Its S(j+1) = K(j+1) Q^T products and the
-  // O^T += V(j-1)^T P(j-1)^T products of the previous tile are interleaved
-  // with the softmax VALU work on S(j). LDS: K(j+1) and V(j-1) are read while
-  // the DMA fills the other buffer of each pair with K(j+2) and V(j); one
-  // barrier per iteration.
-  struct PSet { v8i hi[QB], lo[QB]; };
-  PSet pa, pb;
+  // any probability is formed; its S(j+1) = K(j+1) Q^T products run on the
+  // matrix core while the VALU forms P(j), and the O^T += V(j)^T P(j)^T
+  // products follow at its end. LDS: an iteration reads K(j+1) and V(j) while
+  // the DMA fills the other buffer of each pair with K(j+2) and V(j+1); one
+  // barrier per iteration, at its start.
+  v8i phi[QB], plo[QB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) pb.hi[qb] = pb.lo[qb] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  for (int qb = 0; qb < QB; ++qb) phi[qb] = plo[qb] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
   constexpr int kOne8 = 0x38383838;   // four e4m3 1.0
   // hd128: constant A operand of the ones block (row 0 = 1.0); hd72: the A
   // operand row of column 72 (lanes with i16 == 8 of block 4) is set to 1.0.
@@ -319,13 +316,6 @@ void attn_kernel(AttnArgs a) {
     }
     return r;
   };
-  auto pv_block = [&](const PSet& pp, const v8i& vop, int cb) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      o[qb][cb] = mfma_fp8(vop, pp.hi[qb], o[qb][cb]);
-      o[qb][cb] = mfma_fp8(vop, pp.lo[qb], o[qb][cb]);
-    }
-  };
 
   // S(0)
   v4f sc[QB][8];
@@ -340,18 +330,21 @@ void attn_kernel(AttnArgs a) {
       for (int qb = 0; qb < QB; ++qb) sc[qb][t] = mfma_fp8(kop, qop[qb], zero4);
     }
   }
-  __syncthreads();   // K buffer 0 receives K(2) in iteration 0
 
   // One iteration; LAST: keys of S(j) past the segment end are masked and
   // there is no S(j+1). ODD = j & 1 selects the buffers.
-  auto iteration = [&](auto last_c, auto odd_c, int j, PSet& cur, const PSet& prev) {
+  auto iteration = [&](auto last_c, auto odd_c, int j) {
     constexpr bool LAST = decltype(last_c)::value;
     constexpr bool ODD = decltype(odd_c)::value;
-    uint8_t* const k_fill = ODD ? k_lds1 : k_lds0;     // K(j+2)
-    uint8_t* const v_fill = ODD ? v_lds1 : v_lds0;     // V(j)
+    uint8_t* const k_fill = ODD ? k_lds1 : k_lds0;         // K(j+2)
+    uint8_t* const v_fill = ODD ? v_lds0 : v_lds1;         // V(j+1)
     const uint8_t* const k_read = ODD ? k_lds0 : k_lds1;   // K(j+1)
-    const uint8_t* const v_read = ODD ? v_lds0 : v_lds1;   // V(j-1)
-    dma_tiles(j + 2, k_fill, j, v_fill, true);
+    const uint8_t* const v_read = ODD ? v_lds1 : v_lds0;   // V(j)
+    // The previous iteration's reads of the buffers refilled below are done,
+    // and this wave's DMA of K(j+1) and V(j) has landed, on every wave.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    dma_tiles(j + 2, k_fill, j + 1, v_fill, true);
     if (LAST) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
@@ -362,32 +355,32 @@ void attn_kernel(AttnArgs a) {
             sc[qb][t][r] = (j * kBN + 32 * g + 4 * t + r >= L) ? -INFINITY : sc[qb][t][r];
     }
     // Lazy reference max: only when a score exceeds its row's threshold is the
-    // row max reduced across the four lane groups and m_ref moved. O is
-    // rescaled at the end of the iteration, after the previous tile's
-    // products (formed with the old m_ref) have been added.
+    // row max reduced across the four lane groups, m_ref moved and O rescaled.
     float lm[QB];
     bool over = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float m = -INFINITY;
+      float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-        m = fmaxf(fmaxf(fmaxf(fmaxf(m, sc[qb][t][0]), sc[qb][t][1]), sc[qb][t][2]), sc[qb][t][3]);
-      lm[qb] = m;
-      over = over || (m > thr[qb]);
+      for (int t = 0; t < 8; t += 2) {
+        m0 = fmaxf(fmaxf(fmaxf(fmaxf(m0, sc[qb][t][0]), sc[qb][t][1]), sc[qb][t][2]), sc[qb][t][3]);
+        m1 = fmaxf(fmaxf(fmaxf(fmaxf(m1, sc[qb][t + 1][0]), sc[qb][t + 1][1]), sc[qb][t + 1][2]), sc[qb][t + 1][3]);
+      }
+      lm[qb] = fmaxf(m0, m1);
+      over = over || (lm[qb] > thr[qb]);
     }
-    const bool rescale = __ballot(over) != 0ull;
-    float alpha[QB];
-    if (rescale) {
+    if (__ballot(over) != 0ull) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         float m = lm[qb];
         m = fmaxf(m, __shfl_xor(m, 16, 64));
         m = fmaxf(m, __shfl_xor(m, 32, 64));
         const float mn = fmaxf(mref[qb], m * cexp);
-        alpha[qb] = __builtin_amdgcn_exp2f(mref[qb] - mn);
+        const float alpha = __builtin_amdgcn_exp2f(mref[qb] - mn);
         mref[qb] = mn;
         thr[qb] = (mn + kLazy) / cexp;
+#pragma unroll
+        for (int cb = 0; cb < C::NCB; ++cb) o[qb][cb] *= alpha;
       }
     }
     float nb[QB];
@@ -397,30 +390,18 @@ void attn_kernel(AttnArgs a) {
     uint32_t kbase = (uint32_t)kl_lane, vbase = (uint32_t)vl_lane;
     asm volatile("" : "+v"(kbase), "+v"(vbase));
     const lds_u8* kl = (const lds_u8*)k_read + kbase;
-    const lds_u8* vprev = (const lds_u8*)v_read + vbase;
-    // Operands are read one step ahead of their products; the scheduling
-    // barrier at the end of each step keeps the compiler from hoisting every
-    // LDS read of the iteration to its top (that would cost ~40 VGPRs).
-    v8i kop, vop;
+    const lds_u8* vl = (const lds_u8*)v_read + vbase;
+    // P(j) block by block, each followed by the S(j+1) product of that block
+    // (its K operand read one step ahead).
+    v8i kop;
     if (!LAST) kop = k_operand<D>(kl, 0);
-    vop = v_op(vprev, 0);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      if (t < C::NCB) {
-        const v8i vcur = vop;
-        if (t + 1 < C::NCB) vop = v_op(vprev, t + 1);
-        pv_block(prev, vcur, t);
-      }
-      if (t == 7 && C::NCB > 8) pv_block(prev, ones_op, 8);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const int2 p = probs_to_fp8(sc[qb][t], cexp, nb[qb]);
-        cur.hi[qb][t] = p.x;
-        cur.lo[qb][t] = p.y;
-        // P of this tile is consumed only by the next iteration; pin its
-        // computation here, interleaved with this step's MFMAs, instead of
-        // letting it sink to its use.
-        asm volatile("" : "+v"(cur.hi[qb]), "+v"(cur.lo[qb]));
+        const int2 p = probs_to_fp8(sc[qb][t], cexp, nb[qb], phi[qb][t], plo[qb][t]);
+        phi[qb][t] = p.x;
+        plo[qb][t] = p.y;
       }
       if (!LAST) {
         const v8i kcur = kop;
@@ -428,38 +409,41 @@ void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) sc[qb][t] = mfma_fp8(kcur, qop[qb], zero4);
       }
+      // keep the steps apart: hoisting later LDS reads or softmax work into
+      // this step would raise register pressure
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (rescale) {
+    // O^T += V(j)^T P(j)^T, block cb's lo term issued after block cb+1's hi
+    // term, so no product waits on the one just issued.
+    v8i vprev = v_op(vl, 0);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QB; ++qb) o[qb][0] = mfma_fp8(vprev, phi[qb], o[qb][0]);
 #pragma unroll
-        for (int cb = 0; cb < C::NCB; ++cb) o[qb][cb] *= alpha[qb];
+    for (int cb = 1; cb < C::NCB; ++cb) {
+      const v8i vcur = v_op(vl, cb);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) o[qb][cb] = mfma_fp8(vcur, phi[qb], o[qb][cb]);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) o[qb][cb - 1] = mfma_fp8(vprev, plo[qb], o[qb][cb - 1]);
+      vprev = vcur;
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's DMA of K(j+2), V(j)
-    __syncthreads();
-  };
-  // P.V of the last tile; its V arrived before the last barrier
-  auto final_pv = [&](const PSet& pp, const uint8_t* vbuf) {
-    const lds_u8* vlast = (const lds_u8*)vbuf + vl_lane;
 #pragma unroll
-    for (int cb = 0; cb < C::NCB; ++cb) pv_block(pp, v_op(vlast, cb), cb);
+    for (int qb = 0; qb < QB; ++qb) o[qb][C::NCB - 1] = mfma_fp8(vprev, plo[qb], o[qb][C::NCB - 1]);
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
   int j = 0;
   for (; j + 2 < ntiles; j += 2) {
-    iteration(F_{}, F_{}, j, pa, pb);
-    iteration(F_{}, T_{}, j + 1, pb, pa);
+    iteration(F_{}, F_{}, j);
+    iteration(F_{}, T_{}, j + 1);
   }
   if (j + 1 < ntiles) {
-    iteration(F_{}, F_{}, j, pa, pb);
-    iteration(T_{}, T_{}, j + 1, pb, pa);
-    final_pv(pb, v_lds1);
+    iteration(F_{}, F_{}, j);
+    iteration(T_{}, T_{}, j + 1);
   } else {
-    iteration(T_{}, F_{}, j, pa, pb);
-    final_pv(pa, v_lds0);
+    iteration(T_{}, F_{}, j);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no DMA in flight past the loop
 
   // ---- epilogue: divide by the row sum (ones column), scale by dv, bf16 ----
 #pragma unroll
