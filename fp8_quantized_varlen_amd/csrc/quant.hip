@@ -6,6 +6,14 @@
 // ties to even (the hardware v_cvt_pk_fp8_f32 conversion; its rounding is
 // checked against an exact software model over every bf16 input).
 //
+// The fp32 quotient is formed as RN32(RN64(x * r)) with r = RN64(1/descale),
+// which equals RN32(x / descale) for every bf16 x: the fp64 product is within
+// 2^-52 (relative) of x/descale, while x/descale (8 significant bits over 24)
+// is either an fp32 number or at least 2^-49 (relative) away from every fp32
+// rounding midpoint, which would need 25 significant bits in x. Overflow
+// gives inf on both sides and then 448. Three VALU instructions instead of
+// the ~10 of a correctly rounded fp32 division.
+//
 // Dynamic mode (vLLM page "FP8 ViT Encoder Attention", Usage): the amax of
 // each whole tensor is reduced first, pushed into the 16-slot ring, and the
 // window maximum sets this forward's descale. The amax pass and the quantize
@@ -23,7 +31,13 @@
 namespace fp8vit {
 
 constexpr int kQuantThreads = 512;
-constexpr int kUnroll = 8;
+constexpr int kUnroll = 4;   // chunks per tensor in flight per thread (12 for the three)
+// Dynamic mode: one block of 1024 threads per CU. When every thread's share
+// is at most kResident chunks per tensor (up to 8M elements per tensor on 256
+// CUs), the chunks loaded for the amax stay in registers across the grid
+// barrier and are quantized from there: the input is read once.
+constexpr int kDynThreads = 1024;
+constexpr int kResident = 8;
 // Upper bound on one grid-barrier wait, in ticks of the 100 MHz real-time
 // counter (20 ms). Reaching it means the co-residency assumption failed; the
 // state flag records it and the kernel still runs to completion.
@@ -32,17 +46,22 @@ constexpr uint64_t kBarrierTimeoutTicks = 2000000ull;
 __device__ __forceinline__ uint32_t bf16_lo(uint32_t w) { return w << 16; }
 __device__ __forceinline__ uint32_t bf16_hi(uint32_t w) { return w & 0xffff0000u; }
 
-__device__ __forceinline__ float quant_value(uint32_t fbits, float d) {
-  float q = __fdiv_rn(__uint_as_float(fbits), d);
+// r = RN64(1 / descale), see the header comment.
+__device__ __forceinline__ float quant_value(uint32_t fbits, double r) {
+  const float q = (float)((double)__uint_as_float(fbits) * r);
   return __builtin_amdgcn_fmed3f(q, -kFp8Max, kFp8Max);
 }
 
 // 8 bf16 (one 16-byte chunk) -> 8 e4m3 codes (8 bytes), element order kept.
-__device__ __forceinline__ uint2 quant_chunk(uint4 w, float d) {
-  uint32_t a = __builtin_amdgcn_cvt_pk_fp8_f32(quant_value(bf16_lo(w.x), d), quant_value(bf16_hi(w.x), d), 0, false);
-  a = __builtin_amdgcn_cvt_pk_fp8_f32(quant_value(bf16_lo(w.y), d), quant_value(bf16_hi(w.y), d), a, true);
-  uint32_t b = __builtin_amdgcn_cvt_pk_fp8_f32(quant_value(bf16_lo(w.z), d), quant_value(bf16_hi(w.z), d), 0, false);
-  b = __builtin_amdgcn_cvt_pk_fp8_f32(quant_value(bf16_lo(w.w), d), quant_value(bf16_hi(w.w), d), b, true);
+__device__ __forceinline__ uint2 quant_chunk(uint4 w, double r) {
+  // The first conversion of a pair keeps the upper half of its tied "old"
+  // operand (overwritten by the second): pass the consumed input word.
+  uint32_t a = __builtin_amdgcn_cvt_pk_fp8_f32(quant_value(bf16_lo(w.x), r), quant_value(bf16_hi(w.x), r), (int)w.x,
+                                               false);
+  a = __builtin_amdgcn_cvt_pk_fp8_f32(quant_value(bf16_lo(w.y), r), quant_value(bf16_hi(w.y), r), a, true);
+  uint32_t b = __builtin_amdgcn_cvt_pk_fp8_f32(quant_value(bf16_lo(w.z), r), quant_value(bf16_hi(w.z), r), (int)w.z,
+                                               false);
+  b = __builtin_amdgcn_cvt_pk_fp8_f32(quant_value(bf16_lo(w.w), r), quant_value(bf16_hi(w.w), r), b, true);
   return make_uint2(a, b);
 }
 
@@ -66,43 +85,53 @@ __device__ __forceinline__ const uint4* chunk_src(const uint16_t* x, int64_t ld,
   return reinterpret_cast<const uint4*>(x + (int64_t)t * ld + 8 * (int64_t)j);
 }
 
+// Quantize Q, K and V together: each thread keeps kUnroll chunks of each of
+// the three tensors in flight before converting and storing them.
 template <bool CONTIG>
-__device__ __forceinline__ void quantize_tensor(const uint16_t* __restrict__ x, int64_t ld, uint8_t* __restrict__ y,
-                                                int32_t row8, uint32_t n8, float d, uint32_t gtid,
-                                                uint32_t gstride) {
-  uint2* out = reinterpret_cast<uint2*>(y);
+__device__ __forceinline__ void quantize_all(const QuantArgs& a, uint32_t n8, const double* r, uint32_t gtid,
+                                             uint32_t gstride) {
   for (uint32_t base = gtid; base < n8; base += gstride * kUnroll) {
-    uint4 w[kUnroll];
+    uint4 w[3][kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      uint32_t c = base + u * gstride;
-      w[u] = c < n8 ? *chunk_src<CONTIG>(x, ld, row8, c) : make_uint4(0, 0, 0, 0);
-    }
+    for (int x = 0; x < 3; ++x)
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      uint32_t c = base + u * gstride;
-      if (c < n8) out[c] = quant_chunk(w[u], d);
-    }
+      for (int u = 0; u < kUnroll; ++u) {
+        const uint32_t c = base + u * gstride;
+        w[x][u] = c < n8 ? *chunk_src<CONTIG>(a.x[x], a.ld[x], a.row8, c) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+    for (int x = 0; x < 3; ++x)
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const uint32_t c = base + u * gstride;
+        if (c < n8) reinterpret_cast<uint2*>(a.y[x])[c] = quant_chunk(w[x][u], r[x]);
+      }
   }
 }
 
+// Largest |x| bits of each of Q, K, V over this thread's chunks (the same
+// chunks quantize_all visits), with 3 * kUnroll loads in flight.
 template <bool CONTIG>
-__device__ __forceinline__ uint32_t absmax_tensor(const uint16_t* __restrict__ x, int64_t ld, int32_t row8,
-                                                  uint32_t n8, uint32_t gtid, uint32_t gstride) {
-  uint32_t m = 0;
+__device__ __forceinline__ void absmax_all(const QuantArgs& a, uint32_t n8, uint32_t gtid, uint32_t gstride,
+                                           uint32_t m[3]) {
+  m[0] = m[1] = m[2] = 0;
   for (uint32_t base = gtid; base < n8; base += gstride * kUnroll) {
-    uint4 w[kUnroll];
+    uint4 w[3][kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      uint32_t c = base + u * gstride;
-      w[u] = c < n8 ? *chunk_src<CONTIG>(x, ld, row8, c) : make_uint4(0, 0, 0, 0);
-    }
+    for (int x = 0; x < 3; ++x)
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) m = max(m, chunk_absmax_bits(w[u]));
+      for (int u = 0; u < kUnroll; ++u) {
+        const uint32_t c = base + u * gstride;
+        w[x][u] = c < n8 ? *chunk_src<CONTIG>(a.x[x], a.ld[x], a.row8, c) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+    for (int x = 0; x < 3; ++x)
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) m[x] = max(m[x], chunk_absmax_bits(w[x][u]));
   }
-  return m;
 }
 
+template <int THREADS>
 __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* red) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
@@ -111,7 +140,7 @@ __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* red) {
   __syncthreads();
   uint32_t r = red[0];
 #pragma unroll
-  for (int i = 1; i < kQuantThreads / 64; ++i) r = max(r, red[i]);
+  for (int i = 1; i < THREADS / 64; ++i) r = max(r, red[i]);
   __syncthreads();
   return r;
 }
@@ -144,26 +173,31 @@ __device__ void grid_barrier(DevState* st, uint32_t nblocks) {
 
 template <bool CONTIG>
 __global__ __launch_bounds__(kQuantThreads) void quant_static_kernel(QuantArgs a) {
+  __shared__ double rcp[3];
   const uint32_t gtid = blockIdx.x * kQuantThreads + threadIdx.x;
   const uint32_t gstride = gridDim.x * kQuantThreads;
   const uint32_t n8 = (uint32_t)a.T * (uint32_t)a.row8;
-  float d[3];
+  if (threadIdx.x == 0) {
 #pragma unroll
-  for (int x = 0; x < 3; ++x) d[x] = descale_from_amax(a.st->static_values[x]);
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-#pragma unroll
-    for (int x = 0; x < 3; ++x) a.st->descale_used[x] = d[x];
+    for (int x = 0; x < 3; ++x) {
+      const float d = descale_from_amax(a.st->static_values[x]);
+      rcp[x] = 1.0 / (double)d;
+      if (blockIdx.x == 0) a.st->descale_used[x] = d;
+    }
   }
-#pragma unroll
-  for (int x = 0; x < 3; ++x) quantize_tensor<CONTIG>(a.x[x], a.ld[x], a.y[x], a.row8, n8, d[x], gtid, gstride);
+  __syncthreads();
+  const double r[3] = {rcp[0], rcp[1], rcp[2]};
+  quantize_all<CONTIG>(a, n8, r, gtid, gstride);
 }
 
 template <bool CONTIG>
-__global__ __launch_bounds__(kQuantThreads) void quant_dynamic_kernel(QuantArgs a) {
-  __shared__ uint32_t red[kQuantThreads / 64];
-  const uint32_t gtid = blockIdx.x * kQuantThreads + threadIdx.x;
-  const uint32_t gstride = gridDim.x * kQuantThreads;
+__global__ __launch_bounds__(kDynThreads) void quant_dynamic_kernel(QuantArgs a) {
+  __shared__ uint32_t red[kDynThreads / 64];
+  __shared__ double rcp[3];
+  const uint32_t gtid = blockIdx.x * kDynThreads + threadIdx.x;
+  const uint32_t gstride = gridDim.x * kDynThreads;
   const uint32_t n8 = (uint32_t)a.T * (uint32_t)a.row8;
+  const bool resident = n8 <= gstride * (uint32_t)kResident;   // grid-uniform
   DevState* st = a.st;
   // Ring and count are read before the barrier; block 0 rewrites them after it.
   const uint32_t count = st->count;
@@ -183,31 +217,62 @@ __global__ __launch_bounds__(kQuantThreads) void quant_dynamic_kernel(QuantArgs 
     }
   }
   // Phase A: amax of each tensor.
+  uint4 held[3][kResident];
+  uint32_t mt[3] = {0, 0, 0};
+  if (resident) {
+#pragma unroll
+    for (int x = 0; x < 3; ++x)
+#pragma unroll
+      for (int u = 0; u < kResident; ++u) {
+        const uint32_t c = gtid + u * gstride;
+        held[x][u] = c < n8 ? *chunk_src<CONTIG>(a.x[x], a.ld[x], a.row8, c) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+    for (int x = 0; x < 3; ++x)
+#pragma unroll
+      for (int u = 0; u < kResident; ++u) mt[x] = max(mt[x], chunk_absmax_bits(held[x][u]));
+  } else {
+    absmax_all<CONTIG>(a, n8, gtid, gstride, mt);
+  }
 #pragma unroll
   for (int x = 0; x < 3; ++x) {
-    uint32_t m = absmax_tensor<CONTIG>(a.x[x], a.ld[x], a.row8, n8, gtid, gstride);
-    m = block_max(m, red);
+    const uint32_t m = block_max<kDynThreads>(mt[x], red);
     if (threadIdx.x == 0 && m != 0u)
       __hip_atomic_fetch_max(&st->amax_bits[par][x], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   grid_barrier(st, gridDim.x);
-  // Phase B: descales from the window max including this forward.
-  float amax[3], d[3];
+  // Phase B: descales from the window max including this forward (one
+  // thread per block; the reciprocals go to the block through LDS).
+  if (threadIdx.x == 0) {
+    float amax[3], d[3];
 #pragma unroll
-  for (int x = 0; x < 3; ++x) {
-    uint32_t bits = __hip_atomic_load(&st->amax_bits[par][x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    amax[x] = __uint_as_float(bits << 16);
-    float w = amax[x] > ring_max_other[x] ? amax[x] : ring_max_other[x];
-    d[x] = descale_from_amax(w);
-  }
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    ring_commit(st, count, amax, d);
+    for (int x = 0; x < 3; ++x) {
+      uint32_t bits = __hip_atomic_load(&st->amax_bits[par][x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      amax[x] = __uint_as_float(bits << 16);
+      float w = amax[x] > ring_max_other[x] ? amax[x] : ring_max_other[x];
+      d[x] = descale_from_amax(w);
+      rcp[x] = 1.0 / (double)d[x];
+    }
+    if (blockIdx.x == 0) {
+      ring_commit(st, count, amax, d);
 #pragma unroll
-    for (int x = 0; x < 3; ++x) st->amax_bits[par ^ 1u][x] = 0u;   // scratch of the next forward
+      for (int x = 0; x < 3; ++x) st->amax_bits[par ^ 1u][x] = 0u;   // scratch of the next forward
+    }
   }
+  __syncthreads();
   // Phase C: quantize.
+  const double r[3] = {rcp[0], rcp[1], rcp[2]};
+  if (resident) {
 #pragma unroll
-  for (int x = 0; x < 3; ++x) quantize_tensor<CONTIG>(a.x[x], a.ld[x], a.y[x], a.row8, n8, d[x], gtid, gstride);
+    for (int x = 0; x < 3; ++x)
+#pragma unroll
+      for (int u = 0; u < kResident; ++u) {
+        const uint32_t c = gtid + u * gstride;
+        if (c < n8) reinterpret_cast<uint2*>(a.y[x])[c] = quant_chunk(held[x][u], r[x]);
+      }
+  } else {
+    quantize_all<CONTIG>(a, n8, r, gtid, gstride);
+  }
 }
 
 namespace {
@@ -226,8 +291,8 @@ const DeviceInfo& device_info() {
     hipDeviceProp_t p;
     if (hipGetDeviceProperties(&p, dev) == hipSuccess) {
       int b1 = 0, b2 = 0;
-      (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&b1, quant_dynamic_kernel<true>, kQuantThreads, 0);
-      (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&b2, quant_dynamic_kernel<false>, kQuantThreads, 0);
+      (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&b1, quant_dynamic_kernel<true>, kDynThreads, 0);
+      (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&b2, quant_dynamic_kernel<false>, kDynThreads, 0);
       di.coop_blocks_contig = (b1 > 0 ? b1 : 1) * p.multiProcessorCount;
       di.coop_blocks_strided = (b2 > 0 ? b2 : 1) * p.multiProcessorCount;
       di.cus = p.multiProcessorCount;
@@ -253,19 +318,21 @@ hipError_t launch_quantize(const QuantArgs& a, bool dynamic, hipStream_t s) {
       hipLaunchKernelGGL(quant_static_kernel<false>, dim3((unsigned)g), dim3(kQuantThreads), 0, s, a);
     return hipGetLastError();
   }
-  // One block per CU: a small fraction of what could be resident, so all
-  // blocks are on the chip together while they wait at the grid barrier (the
-  // cooperative launch also refuses grids that could not be).
-  uint64_t g = want < 1 ? 1 : want;
+  // At most one block per CU, all on the chip together while they wait at the
+  // grid barrier (the cooperative launch refuses grids that could not be);
+  // just enough blocks for the register-resident path when it applies.
+  const uint64_t per_block = (uint64_t)kDynThreads * kResident;
+  uint64_t g = (n8 + per_block - 1) / per_block;
+  if (g < 1) g = 1;
   uint64_t cap = (uint64_t)di.cus;
-  const uint64_t resident = (uint64_t)(contig ? di.coop_blocks_contig : di.coop_blocks_strided);
-  if (cap > resident) cap = resident;
+  const uint64_t coresident = (uint64_t)(contig ? di.coop_blocks_contig : di.coop_blocks_strided);
+  if (cap > coresident) cap = coresident;
   if (g > cap) g = cap;
   QuantArgs args = a;
   void* params[] = {&args};
   const void* fn = contig ? reinterpret_cast<const void*>(quant_dynamic_kernel<true>)
                           : reinterpret_cast<const void*>(quant_dynamic_kernel<false>);
-  return hipLaunchCooperativeKernel(fn, dim3((unsigned)g), dim3(kQuantThreads), params, 0, s);
+  return hipLaunchCooperativeKernel(fn, dim3((unsigned)g), dim3(kDynThreads), params, 0, s);
 }
 
 }  // namespace fp8vit
