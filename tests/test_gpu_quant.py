@@ -46,6 +46,39 @@ def test_quantize_static_exhaustive_bf16():
         assert s["count"] == 0 and s["ring"] == [[0.0] * 16] * 3
 
 
+def _random_static_values(n=60, seed=7):
+    """Seeded fp32 file values with random 24-bit mantissas over 18 decades,
+    plus neighbours of powers of two and of 448 * 2^k."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    vals = list((10.0 ** rng.uniform(-9, 9, n)).astype(np.float32))
+    for k in (-20, -3, 0, 5, 17):
+        p = np.float32(2.0 ** k)
+        vals += [np.nextafter(p, np.float32(0)), p, np.nextafter(p, np.float32(np.inf)), np.float32(448.0) * p]
+    return [float(v) for v in vals]
+
+
+def test_quantize_static_exhaustive_bf16_random_descales():
+    """Every finite bf16 pattern against many unrelated descales: the kernel's
+    quotient RN32(x * RN64(1/descale)) must equal the IEEE fp32 division."""
+    dev = require_gpu()
+    xs = [_all_bf16_tensor(s) for s in (0, 7, 333)]
+    td = [to_dev(x, dev) for x in xs]
+    st = fv.new_state(dev)
+    vals_all = _random_static_values()
+    for i in range(0, len(vals_all) - 2, 3):
+        vals = vals_all[i:i + 3]
+        fv.state_set_static(st, vals)
+        codes = fv.quantize_qkv(td[0], td[1], td[2], st, "static")
+        torch.cuda.synchronize()
+        ds = oracle.scales.static_descales(vals)
+        for x, c, d in zip(xs, codes, ds):
+            ref = oracle.quant.quantize(x, d)
+            got = codes_np(c)
+            bad = np.nonzero(got.ravel() != ref.ravel())[0]
+            assert bad.size == 0, f"descale {d!r}: {bad.size} mismatches, first input bits " \
+                                  f"{hex(int(x.ravel()[bad[0]]))} got {hex(got.ravel()[bad[0]])} want {hex(ref.ravel()[bad[0]])}"
+
+
 def test_quantize_dynamic_sequence_matches_ring():
     dev = require_gpu()
     st = fv.new_state(dev)
