@@ -123,12 +123,14 @@ def cpu_baseline(w, qb, kb, vb, static_values, out_gpu, target_s, compare=True):
     est_step = t_quant + w.flops / rate
     work_s = t_quant + pilot
     if est_step <= 30.0:
-        reps = max(1, int(target_s // est_step))
+        # whole steps until target_s of CPU work, never past 30 s
+        reps, elapsed = 0, 0.0
         t0 = time.perf_counter()
-        for _ in range(reps):
+        while reps == 0 or (elapsed < target_s and elapsed + elapsed / reps <= 30.0):
             deq = quantize()
             rows_out = attend(deq, 1 << 30)
-        elapsed = time.perf_counter() - t0
+            reps += 1
+            elapsed = time.perf_counter() - t0
         work_s += elapsed
         value = reps * w.flops / elapsed / 1e12
         sample = (f"{reps} whole step(s): oracle quantization of all {3 * qb.size} elements + fp64 attention "
