@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle baseline")
     p.add_argument("--static-values", default=None,
                    help="q,k,v static values to use instead of calibrating (profiling runs: no dynamic passes)")
+    p.add_argument("--out", choices=("bf16", "fp8"), default="bf16",
+                   help="attention output: bf16, or e4m3 with a static output descale (fused fp8 output)")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 256 MiB device copy (for scaling HBM byte counters)")
     return p.parse_args()
@@ -216,12 +218,20 @@ def main():
     sets = [base] + [[torch.roll(x, shifts=(i * 997) % max(T, 1), dims=0) for x in base] for i in range(1, n_sets)]
     q8, k8, v8 = (torch.empty((T, H, d), dtype=torch.uint8, device=dev) for _ in range(3))
     out = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+    out8 = torch.empty((T, H, d), dtype=torch.uint8, device=dev) if args.out == "fp8" else None
+    out_descale = torch.tensor([0.0025], dtype=torch.float32, device=dev)
+
+    def attend():
+        if out8 is not None:
+            fv.attn_varlen_fp8out(q8, k8, v8, cu, max_seqlen, st, out_descale, out=out8)
+        else:
+            fv.attn_varlen(q8, k8, v8, cu, max_seqlen, st, out=out)
     torch.cuda.synchronize()
 
     def step(i):
         q, k, v = sets[i % n_sets]
         fv.quantize_qkv(q, k, v, st, w.mode, out=(q8, k8, v8))
-        fv.attn_varlen(q8, k8, v8, cu, max_seqlen, st, out=out)
+        attend()
 
     for i in range(args.warmup):
         step(i)
@@ -236,7 +246,7 @@ def main():
         ev[i][0].record()
         fv.quantize_qkv(q, k, v, st, w.mode, out=(q8, k8, v8))
         ev[i][1].record()
-        fv.attn_varlen(q8, k8, v8, cu, max_seqlen, st, out=out)
+        attend()
         ev[i][2].record()
     end.record()
     torch.cuda.synchronize()
@@ -273,7 +283,7 @@ def main():
         "vs_baseline": round(value / PAGE_MI300X_TFLOPS[w.name], 3) if w.name in PAGE_MI300X_TFLOPS else None,
         "dtype": "fp8e4m3",
         "data": "synthetic",
-        "config": {"workload": w.name, "segments": list(w.seglens), "heads": H, "head_dim": d,
+        "config": {"workload": w.name, "segments": list(w.seglens), "heads": H, "head_dim": d, "output": args.out,
                    "scaling": w.mode + (" (1.5 x calibrated)" if w.mode == "static" else " (16-slot ring)"),
                    "outlier_frac": w.outlier_frac, "input_sets_rotated": n_sets},
         "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
@@ -290,6 +300,8 @@ def main():
     if not args.no_cpu_baseline:
         # one more step on the unrotated input, so the oracle rows can be compared with it
         step(0)
+        if out8 is not None:     # the oracle check reads the bf16 output of the same input
+            fv.attn_varlen(q8, k8, v8, cu, max_seqlen, st, out=out)
         torch.cuda.synchronize()
         out_np = out.float().cpu().numpy()
         # dynamic mode: the GPU ring holds only this input's amax (the scales the oracle's

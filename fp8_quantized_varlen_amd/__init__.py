@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "LIB_PATH", "FP8VIT_DYNAMIC", "FP8VIT_STATIC", "Fp8VitError",
     "state_bytes", "new_state", "state_init", "state_set_static", "scales_update",
-    "quantize_qkv", "attn_varlen", "state_read", "load_static_scales", "status_str",
+    "quantize_qkv", "attn_varlen", "attn_varlen_fp8out", "state_read", "load_static_scales", "status_str",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8vit.so")
@@ -45,6 +45,8 @@ _SIGS = {
                                            _vp, _vp, _vp, _vp, _vp]),
     "fp8vit_attn_varlen": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
                                           _vp, _i64, _vp]),
+    "fp8vit_attn_varlen_fp8out": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
+                                                 _vp, _vp, _i64, _vp]),
     "fp8vit_state_read": (ctypes.c_int, [_vp, ctypes.POINTER(_StateView), _vp]),
     "fp8vit_status_str": (ctypes.c_char_p, [ctypes.c_int]),
 }
@@ -163,6 +165,25 @@ def attn_varlen(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, cu_seqlens
                                  int(max_seqlen), T, H, d, float(softmax_scale), _ptr(state), _ptr(out), ld_out,
                                  _stream(q8.device))
     _check("fp8vit_attn_varlen", st)
+    return out
+
+
+def attn_varlen_fp8out(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, cu_seqlens: torch.Tensor,
+                       max_seqlen: int, state: torch.Tensor, out_descale: torch.Tensor, softmax_scale: float = 0.0,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """As attn_varlen, with e4m3 codes of O / out_descale (device float32[1]) as uint8 [T, H, d]."""
+    T, H, d = q8.shape
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 device tensor")
+    if out_descale.dtype != torch.float32 or out_descale.numel() != 1:
+        raise ValueError("out_descale must be a float32 device tensor of one element")
+    if out is None:
+        out = torch.empty((T, H, d), dtype=torch.uint8, device=q8.device)
+    ld_out = out.stride(0) if T > 0 else H * d
+    st = _lib.fp8vit_attn_varlen_fp8out(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(cu_seqlens), cu_seqlens.numel() - 1,
+                                        int(max_seqlen), T, H, d, float(softmax_scale), _ptr(state),
+                                        _ptr(out_descale), _ptr(out), ld_out, _stream(q8.device))
+    _check("fp8vit_attn_varlen_fp8out", st)
     return out
 
 

@@ -74,11 +74,14 @@ fp8vit_status fp8vit_quantize_qkv(const void* q, const void* k, const void* v, i
   return from_hip(fp8vit::launch_quantize(a, mode == FP8VIT_DYNAMIC, as_stream(stream)));
 }
 
-fp8vit_status fp8vit_attn_varlen(const void* q8, const void* k8, const void* v8, const int32_t* d_cu_seqlens,
-                                 int32_t num_segments, int32_t max_seqlen, int32_t total_tokens, int32_t num_heads,
-                                 int32_t head_dim, float softmax_scale, const void* d_state, void* out,
-                                 int64_t ld_out, void* stream) {
+namespace {
+// Shared validation and launch of the bf16- and e4m3-output entry points.
+fp8vit_status attn_common(const void* q8, const void* k8, const void* v8, const int32_t* d_cu_seqlens,
+                          int32_t num_segments, int32_t max_seqlen, int32_t total_tokens, int32_t num_heads,
+                          int32_t head_dim, float softmax_scale, const void* d_state, void* out, bool out_fp8,
+                          const float* d_out_descale, int64_t ld_out, void* stream) {
   if (!d_cu_seqlens || !d_state) return FP8VIT_ERR_INVALID_ARGUMENT;
+  if (out_fp8 && !d_out_descale) return FP8VIT_ERR_INVALID_ARGUMENT;
   if (num_segments < 0 || max_seqlen < 0 || total_tokens < 0 || num_heads <= 0) return FP8VIT_ERR_INVALID_ARGUMENT;
   // Empty tensors may come with null data pointers.
   if (total_tokens > 0 && (!q8 || !k8 || !v8 || !out)) return FP8VIT_ERR_INVALID_ARGUMENT;
@@ -87,8 +90,8 @@ fp8vit_status fp8vit_attn_varlen(const void* q8, const void* k8, const void* v8,
   const int64_t row = (int64_t)num_heads * head_dim;
   if (ld_out < row) return FP8VIT_ERR_INVALID_ARGUMENT;
   if (ld_out % 4) return FP8VIT_ERR_UNSUPPORTED;
-  if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(out, 8) || !aligned(d_cu_seqlens, 4) ||
-      !aligned(d_state, 256))
+  if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(out, out_fp8 ? 4 : 8) ||
+      !aligned(d_cu_seqlens, 4) || !aligned(d_state, 256) || (out_fp8 && !aligned(d_out_descale, 4)))
     return FP8VIT_ERR_UNSUPPORTED;
   if (num_segments == 0 || total_tokens == 0 || max_seqlen == 0) return FP8VIT_OK;  // no rows to write
   const int bm = fp8vit::attn_block_m(head_dim);
@@ -109,10 +112,30 @@ fp8vit_status fp8vit_attn_varlen(const void* q8, const void* k8, const void* v8,
   a.ntiles_ub = (int32_t)ntiles;
   a.tensor_bytes = (uint32_t)((int64_t)total_tokens * row);
   a.st = static_cast<const DevState*>(d_state);
-  a.out = static_cast<uint16_t*>(out);
+  a.out = out_fp8 ? nullptr : static_cast<uint16_t*>(out);
+  a.out8 = out_fp8 ? static_cast<uint8_t*>(out) : nullptr;
+  a.out_descale = d_out_descale;
   a.ld_out = ld_out;
   a.softmax_scale = softmax_scale > 0.0f ? softmax_scale : (float)(1.0 / std::sqrt((double)head_dim));
   return from_hip(fp8vit::launch_attn(a, head_dim, total_tokens, as_stream(stream)));
+}
+}  // namespace
+
+fp8vit_status fp8vit_attn_varlen(const void* q8, const void* k8, const void* v8, const int32_t* d_cu_seqlens,
+                                 int32_t num_segments, int32_t max_seqlen, int32_t total_tokens, int32_t num_heads,
+                                 int32_t head_dim, float softmax_scale, const void* d_state, void* out,
+                                 int64_t ld_out, void* stream) {
+  return attn_common(q8, k8, v8, d_cu_seqlens, num_segments, max_seqlen, total_tokens, num_heads, head_dim,
+                     softmax_scale, d_state, out, false, nullptr, ld_out, stream);
+}
+
+fp8vit_status fp8vit_attn_varlen_fp8out(const void* q8, const void* k8, const void* v8,
+                                        const int32_t* d_cu_seqlens, int32_t num_segments, int32_t max_seqlen,
+                                        int32_t total_tokens, int32_t num_heads, int32_t head_dim,
+                                        float softmax_scale, const void* d_state, const float* d_out_descale,
+                                        void* out8, int64_t ld_out8, void* stream) {
+  return attn_common(q8, k8, v8, d_cu_seqlens, num_segments, max_seqlen, total_tokens, num_heads, head_dim,
+                     softmax_scale, d_state, out8, true, d_out_descale, ld_out8, stream);
 }
 
 fp8vit_status fp8vit_state_read(const void* d_state, fp8vit_state_view* out, void* stream) {

@@ -171,7 +171,7 @@ __device__ __forceinline__ void dma_issue(__amdgpu_buffer_rsrc_t krs, __amdgpu_b
   }
 }
 
-template <int D>
+template <int D, bool OUT8>
 __global__ __launch_bounds__(64 * Cfg<D>::WAVES) __attribute__((amdgpu_waves_per_eu(Cfg<D>::MIN_WAVES_PER_EU)))
 void attn_kernel(AttnArgs a) {
   using C = Cfg<D>;
@@ -445,23 +445,38 @@ void attn_kernel(AttnArgs a) {
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no DMA in flight past the loop
 
-  // ---- epilogue: divide by the row sum (ones column), scale by dv, bf16 ----
+  // ---- epilogue: divide by the row sum (ones column), scale by dv; bf16 RNE,
+  // or e4m3 of O / out_descale (the input formula: fp32 quotient, formed as
+  // RN32(O * RN64(1/out_descale)) which equals the IEEE fp32 division for
+  // fp32 O, clamp to +-448, nearest-even code) ----
+  double out_rcp = 0.0;
+  if (OUT8) out_rcp = 1.0 / (double)(*a.out_descale);
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lsum = __shfl(o[qb][C::ONES_CB][0], C::ONES_LANE0 + i16, 64);
     const float f = dv / lsum;
     const int qr = q0 + wave * BMW + qb * 16 + i16;
     if (qr < L) {
-      uint16_t* dst = a.out + (int64_t)(s0 + qr) * a.ld_out + (int64_t)h * D;
+      const int64_t row = (int64_t)(s0 + qr) * a.ld_out + (int64_t)h * D;
 #pragma unroll
       for (int cb = 0; cb < C::NCB; ++cb) {
         const int col = 16 * cb + 4 * g;
         if (col + 4 <= D) {
           const v4f x = o[qb][cb] * f;
-          uint2 pk;
-          pk.x = bf16_rne(x[0]) | (bf16_rne(x[1]) << 16);
-          pk.y = bf16_rne(x[2]) | (bf16_rne(x[3]) << 16);
-          *reinterpret_cast<uint2*>(dst + col) = pk;
+          if (OUT8) {
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              y[e] = __builtin_amdgcn_fmed3f((float)((double)x[e] * out_rcp), -kFp8Max, kFp8Max);
+            int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+            w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
+            *reinterpret_cast<int*>(a.out8 + row + col) = w;
+          } else {
+            uint2 pk;
+            pk.x = bf16_rne(x[0]) | (bf16_rne(x[1]) << 16);
+            pk.y = bf16_rne(x[2]) | (bf16_rne(x[3]) << 16);
+            *reinterpret_cast<uint2*>(a.out + row + col) = pk;
+          }
         }
       }
     }
@@ -475,10 +490,18 @@ hipError_t launch_attn(const AttnArgs& a, int head_dim, int total_tokens, hipStr
   const int64_t grid = ((items + 7) / 8) * 8;
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   (void)total_tokens;
-  if (head_dim == 72)
-    hipLaunchKernelGGL(attn_kernel<72>, dim3((unsigned)grid), dim3(64 * Cfg<72>::WAVES), 0, s, a);
-  else
-    hipLaunchKernelGGL(attn_kernel<128>, dim3((unsigned)grid), dim3(64 * Cfg<128>::WAVES), 0, s, a);
+  const bool out8 = a.out8 != nullptr;
+  if (head_dim == 72) {
+    if (out8)
+      hipLaunchKernelGGL((attn_kernel<72, true>), dim3((unsigned)grid), dim3(64 * Cfg<72>::WAVES), 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_kernel<72, false>), dim3((unsigned)grid), dim3(64 * Cfg<72>::WAVES), 0, s, a);
+  } else {
+    if (out8)
+      hipLaunchKernelGGL((attn_kernel<128, true>), dim3((unsigned)grid), dim3(64 * Cfg<128>::WAVES), 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_kernel<128, false>), dim3((unsigned)grid), dim3(64 * Cfg<128>::WAVES), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -54,8 +54,10 @@ struct AttnArgs {
   int32_t ntiles_ub;     // upper bound on query tiles per head
   uint32_t tensor_bytes; // T * H * d: bytes of each of q8, k8, v8
   const DevState* st;
-  uint16_t* out;
-  int64_t ld_out;
+  uint16_t* out;           // bf16 output (out8 == nullptr)
+  uint8_t* out8;           // e4m3 output, or nullptr
+  const float* out_descale;  // device fp32, with out8
+  int64_t ld_out;          // token stride of the output, elements
   float softmax_scale;
 };
 hipError_t launch_attn(const AttnArgs& a, int head_dim, int total_tokens, hipStream_t s);

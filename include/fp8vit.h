@@ -155,6 +155,25 @@ fp8vit_status fp8vit_attn_varlen(const void* q8, const void* k8, const void* v8,
                                  int32_t head_dim, float softmax_scale, const void* d_state,
                                  void* out, int64_t ld_out, void* stream);
 
+/* fp8vit_attn_varlen with an e4m3 output, to feed an FP8 output projection
+ * without a separate quantization pass (the fused fp8-output request on the
+ * vLLM issue page "Add support for fused fp8 output to FlashAttention 3").
+ *   d_out_descale device fp32[1]: the output's static per-tensor descale s
+ *                 (finite, > 0; read on the device, so it may change between
+ *                 calls without a host sync).
+ *   out8          e4m3 [total_tokens, H, d], token stride ld_out8 (bytes,
+ *                 >= H*d, multiple of 4), 4-byte aligned.
+ * Each element is the input quantization formula applied to the attention
+ * output O as formed in fp32: e4m3 RNE of clamp(fp32(O / s), +-448). Other
+ * arguments and errors as fp8vit_attn_varlen (ERR_INVALID_ARGUMENT also for a
+ * null d_out_descale). */
+fp8vit_status fp8vit_attn_varlen_fp8out(const void* q8, const void* k8, const void* v8,
+                                        const int32_t* d_cu_seqlens, int32_t num_segments,
+                                        int32_t max_seqlen, int32_t total_tokens, int32_t num_heads,
+                                        int32_t head_dim, float softmax_scale, const void* d_state,
+                                        const float* d_out_descale, void* out8, int64_t ld_out8,
+                                        void* stream);
+
 /* Synchronous read-back of a state for tests and calibration (copies on
  * `stream`, then waits for it). Not for the hot path. */
 fp8vit_status fp8vit_state_read(const void* d_state, fp8vit_state_view* out, void* stream);

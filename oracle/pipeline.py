@@ -49,6 +49,15 @@ def forward(q, k, v, cu_seqlens, mode: str, ring: Optional[scales.AmaxRing] = No
     return ForwardResult(codes, ds, a, out)
 
 
+def quantize_output(out: np.ndarray, out_descale) -> np.ndarray:
+    """FP8 output of the attention (the fused fp8-output feature request on the
+    vLLM issue page "Add support for fused fp8 output to FlashAttention 3"):
+    the per-tensor input formula applied to O. Reading: O is first rounded to
+    fp32, the precision the kernel forms it in, then divided by the static
+    output descale (IEEE fp32), clamped to +-448 and rounded to e4m3."""
+    return quant.quantize_f32(np.asarray(out, dtype=np.float64).astype(np.float32), out_descale)
+
+
 def reference_unquantized(q, k, v, cu_seqlens, softmax_scale=None) -> np.ndarray:
     """Attention on the bf16 values themselves (no quantization), fp64."""
     return attention.attention(quant.bf16_to_f32(q), quant.bf16_to_f32(k), quant.bf16_to_f32(v),

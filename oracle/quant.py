@@ -36,14 +36,20 @@ def amax(bits: np.ndarray) -> np.float32:
     return np.float32(np.max(np.abs(x)))
 
 
-def quantize(bits: np.ndarray, descale) -> np.ndarray:
-    """e4m3 codes of x / descale, clamped to +-448 then rounded to nearest even."""
-    x = bf16_to_f32(bits)
+def quantize_f32(x: np.ndarray, descale) -> np.ndarray:
+    """e4m3 codes of the fp32 values x / descale (IEEE fp32 division), clamped to
+    +-448 then rounded to nearest even."""
+    x = np.asarray(x, dtype=np.float32)
     d = np.float32(descale)
     with np.errstate(over="ignore"):
         y = (x / d).astype(np.float32)
     y = np.clip(y, -e4m3.E4M3_MAX, e4m3.E4M3_MAX).astype(np.float32)
     return e4m3.encode_rne(y)
+
+
+def quantize(bits: np.ndarray, descale) -> np.ndarray:
+    """e4m3 codes of x / descale for bf16 bit patterns x."""
+    return quantize_f32(bf16_to_f32(bits), descale)
 
 
 def dequantize(codes: np.ndarray, descale) -> np.ndarray:

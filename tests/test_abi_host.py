@@ -19,7 +19,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libfp8vit.so no
 def header_functions():
     txt = open(HEADER).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(fp8vit_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(fp8vit_[a-z0-9_]+)\s*\(", txt)))
 
 
 @pytest.fixture(scope="module")
@@ -29,7 +29,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -70,6 +70,15 @@ def test_argument_validation_before_any_hip_call(lib):
     assert a(fake, fake, fake, fake, 1, 10, 10, 16, 72, 0.0, vp(0x10010), fake, 1152, null) == 2
     # empty problems are a no-op that never touches the device
     assert a(fake, fake, fake, fake, 0, 0, 0, 16, 72, 0.0, fake, fake, 1152, null) == 0
+    f8 = lib.fp8vit_attn_varlen_fp8out
+    f8.argtypes = [vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                   ctypes.c_float, vp, vp, vp, ctypes.c_int64, vp]
+    assert f8(fake, fake, fake, fake, 1, 10, 10, 16, 72, 0.0, fake, null, fake, 1152, null) == 1   # no descale
+    assert f8(fake, fake, fake, fake, 1, 10, 10, 16, 72, 0.0, fake, vp(0x10002), fake, 1152, null) == 2
+    assert f8(fake, fake, fake, fake, 1, 10, 10, 16, 72, 0.0, fake, fake, vp(0x10002), 1152, null) == 2
+    assert f8(fake, fake, fake, fake, 1, 10, 10, 16, 72, 0.0, fake, fake, fake, 1150, null) == 1
+    assert f8(fake, fake, fake, fake, 1, 10, 10, 16, 128, 0.0, fake, fake, fake, 2050, null) == 2
+    assert f8(fake, fake, fake, fake, 0, 0, 0, 16, 72, 0.0, fake, fake, fake, 1152, null) == 0
     s = lib.fp8vit_state_set_static
     s.argtypes = [vp, ctypes.POINTER(ctypes.c_float), vp]
     for bad in ([0.0, 1.0, 1.0], [1.0, -2.0, 1.0], [1.0, 1.0, float("inf")], [float("nan"), 1.0, 1.0]):

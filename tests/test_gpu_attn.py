@@ -162,3 +162,96 @@ def test_attention_full_size_packed_outliers():
     (the oracle does too); the kernel must track the oracle there."""
     r_gpu, r_oracle, _ = _workload_case("packed_3x14400_8x1024_hd72", n_rows=192)
     assert r_gpu <= r_oracle * 1.1 + 1e-3, (r_gpu, r_oracle)
+
+
+def _run_fp8out(qb, kb, vb, cu, dev, out_descale, mode="dynamic", static_values=None):
+    st = fv.new_state(dev)
+    if mode == "static":
+        fv.state_set_static(st, static_values)
+    q8, k8, v8 = fv.quantize_qkv(to_dev(qb, dev), to_dev(kb, dev), to_dev(vb, dev), st, mode)
+    T, H, d = qb.shape
+    cu_d = torch.from_numpy(np.asarray(cu, np.int32)).to(dev)
+    seglens = np.diff(cu)
+    maxlen = int(seglens.max()) if len(seglens) else 0
+    s_d = torch.tensor([out_descale], dtype=torch.float32, device=dev)
+    out8 = torch.full((T, H, d), 0x7F, dtype=torch.uint8, device=dev)        # NaN code as canary
+    out8 = fv.attn_varlen_fp8out(q8, k8, v8, cu_d, maxlen, st, s_d, out=out8)
+    o16 = fv.attn_varlen(q8, k8, v8, cu_d, maxlen, st)
+    torch.cuda.synchronize()
+    return codes_np(out8), o16.float().cpu().numpy().astype(np.float64), (q8, k8, v8)
+
+
+def _check_fp8_output(codes8, o16, ref_out, out_descale, vmax):
+    """Bars for the e4m3 output: every element written; decoded values within
+    the attention tolerance plus e4m3's half step of the oracle's O; codes equal
+    to the oracle's fp8 output except for neighbouring codes where O sits at a
+    rounding boundary; and the same codes as the kernel's own bf16 output run
+    through the quantization formula, up to neighbouring codes."""
+    assert not np.any((codes8 & 0x7F) == 0x7F), "unwritten or NaN elements"
+    s = np.float64(np.float32(out_descale))
+    dec = oracle.e4m3.decode(codes8) * s
+    clipped = np.clip(ref_out, -448.0 * s, 448.0 * s)       # the formula saturates at +-448
+    bound = ATOL_FRAC_OF_VMAX * vmax + np.abs(clipped) * 2.0 ** -4 + 2.0 ** -10 * s
+    assert np.all(np.abs(dec - clipped) <= bound)
+    want = oracle.pipeline.quantize_output(ref_out, out_descale)
+
+    def step_distance(a, b):
+        # distance in e4m3 steps for codes of one sign (magnitudes are monotonic in the code)
+        sa = np.where(a & 0x80, -1, 1) * (a & 0x7F).astype(np.int32)
+        sb = np.where(b & 0x80, -1, 1) * (b & 0x7F).astype(np.int32)
+        return np.abs(sa - sb)
+    # where the attention tolerance is well under half an e4m3 step (|O| >= 32 atol),
+    # the kernel's codes are the oracle's or a neighbour at a rounding boundary
+    sure = np.abs(ref_out) >= 32 * ATOL_FRAC_OF_VMAX * vmax
+    d1 = step_distance(codes8, want)[sure]
+    assert d1.size == 0 or (d1.max() <= 1 and d1.mean() <= 0.02), (d1.max(), d1.mean())
+    own = oracle.quant.quantize_f32(o16.astype(np.float32), out_descale)
+    d2 = step_distance(codes8, own)
+    assert d2.max() <= 1 and d2.mean() <= 0.05, (d2.max(), d2.mean())   # bf16 rounding can cross an e4m3 boundary
+
+
+@pytest.mark.parametrize("seglens,d", [((1, 0, 200, 129, 0, 7), 72), ((300,), 72), ((129, 1, 17), 128)])
+def test_attention_fp8_output_small(seglens, d):
+    dev = require_gpu()
+    cu = make_cu_seqlens(seglens)
+    qb, kb, vb = make_qkv(sum(seglens) * 3 + d, int(cu[-1]), 3, d)
+    ref = oracle.pipeline.forward(qb, kb, vb, cu, "dynamic", ring=oracle.scales.AmaxRing())
+    out_descale = float(np.float32(np.abs(ref.out).max() / 300.0))
+    codes8, o16, codes = _run_fp8out(qb, kb, vb, cu, dev, out_descale)
+    for c, r in zip(codes, ref.codes):
+        assert np.array_equal(codes_np(c), r)
+    _check_fp8_output(codes8, o16, ref.out, out_descale, vmax_of(vb))
+
+
+def test_attention_fp8_output_saturates_and_scales():
+    """A descale too small for the output: every large element saturates to
+    +-448 codes (0x7E / 0xFE), never NaN; a descale of 2x halves the codes' values."""
+    dev = require_gpu()
+    cu = make_cu_seqlens((64, 130))
+    qb, kb, vb = make_qkv(77, 194, 2, 72)
+    ref = oracle.pipeline.forward(qb, kb, vb, cu, "dynamic", ring=oracle.scales.AmaxRing())
+    tiny = float(np.float32(np.abs(ref.out).max() / 1e5))
+    codes8, o16, _ = _run_fp8out(qb, kb, vb, cu, dev, tiny)
+    big = np.abs(ref.out) / tiny > 500
+    assert np.all((codes8[big] & 0x7F) == 0x7E)
+    _check_fp8_output(codes8, o16, ref.out, tiny, vmax_of(vb))
+
+
+def test_attention_fp8_output_full_size_sampled():
+    dev = require_gpu()
+    w = WORKLOADS["l8192_hd72_static"]
+    qb, kb, vb = w.inputs()
+    cu = w.cu_seqlens
+    static_values = oracle.pipeline.calibrate([w.inputs(s) for s in w.warm_seeds[:4]], 1.5)
+    out_descale = 0.0025
+    codes8, o16, codes = _run_fp8out(qb, kb, vb, cu, dev, out_descale, "static", static_values)
+    ds = np.float32(oracle.scales.static_descales(static_values))
+    rng = np.random.default_rng(1)
+    T, H, d = qb.shape
+    rows = list(zip(rng.integers(0, T, 256).tolist(), rng.integers(0, H, 256).tolist())) + [(0, 0), (T - 1, H - 1)]
+    deq = [oracle.quant.dequantize(codes_np(c), s) for c, s in zip(codes, ds)]
+    ref = oracle.attention.attention_rows(deq[0], deq[1], deq[2], cu, rows)
+    got8 = np.stack([codes8[t, h] for t, h in rows])
+    got16 = np.stack([o16[t, h] for t, h in rows])
+    _check_fp8_output(got8, got16, ref, out_descale, vmax_of(vb))
+    assert not np.any((codes8 & 0x7F) == 0x7F)

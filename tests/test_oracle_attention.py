@@ -156,3 +156,18 @@ def test_calibration_values():
     for j in range(3):
         m = max(quant.amax(d[j]) for d in draws)
         assert vals[j] == np.float32(np.float32(1.5) * m)
+
+
+def test_output_quantization_is_the_input_formula_on_fp32_O():
+    """pipeline.quantize_output: O rounded to fp32, then the per-tensor formula."""
+    import oracle
+    rng = np.random.default_rng(9)
+    out = rng.standard_normal((37, 3, 8)) * 0.3
+    s = np.float32(0.0021)
+    codes = oracle.pipeline.quantize_output(out, s)
+    assert codes.shape == out.shape and codes.dtype == np.uint8
+    assert np.array_equal(codes, oracle.quant.quantize_f32(out.astype(np.float32), s))
+    # round trip: decoding lands within half an e4m3 step (3 mantissa bits) of O
+    dec = oracle.e4m3.decode(codes) * np.float64(s)
+    big = np.abs(out) > 2.0 ** -6 * float(s)
+    assert np.all(np.abs(dec - out)[big] <= np.abs(out)[big] * 2.0 ** -4 * 1.0001)

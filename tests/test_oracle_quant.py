@@ -109,3 +109,23 @@ def test_dequantize_exact():
     fin = ~np.isnan(v)
     for c in np.nonzero(fin)[0][::7]:
         assert Fraction(float(v[c])) == Fraction(float(e4m3.DECODE_TABLE[c])) * Fraction(float(d))
+
+
+def test_quantize_f32_matches_torch_formula_and_exact_rationals():
+    """quantize_f32 (used for the fp8 attention output) on fp32 values with full
+    24-bit mantissas: torch's float8 cast of the same formula, and the exact
+    rational reference on a sample."""
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(20000) * 10.0 ** rng.uniform(-6, 4, 20000)).astype(np.float32)
+    x = np.concatenate([x, np.float32([0.0, -0.0, 448.0, -1e30, 3.4e38])])
+    for d in (np.float32(1e-10), np.float32(0.0123456), np.float32(3.3333333), np.float32(0.5)):
+        ours = quant.quantize_f32(x, d)
+        ref = (torch.from_numpy(x) / torch.tensor(d)).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+        assert np.array_equal(ours, ref.view(torch.uint8).numpy())
+        for xi, gi in zip(x[:300], ours[:300]):
+            assert gi == _exact_code(float(xi), d), (xi, d, gi)
+
+
+def test_quantize_f32_agrees_with_bf16_path():
+    for d in DESCALES:
+        assert np.array_equal(quant.quantize_f32(quant.bf16_to_f32(FINITE_BF16), d), quant.quantize(FINITE_BF16, d))
