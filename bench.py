@@ -62,22 +62,19 @@ def to_dev(bits, dev):
 
 
 def calibrate_static(fv, w, dev, margin=1.5):
-    """Calibrate-once: 16 dynamic passes on calibration draws, save margin x window
-    max to a JSON scale file, read it back through the library's loader."""
-    import numpy as np
+    """Calibrate-once: 16 dynamic passes on calibration draws, then the library
+    saves margin x window max to a JSON scale file and reads it back."""
     cal = fv.new_state(dev)
     for s in w.warm_seeds:
         q, k, v = (to_dev(x, dev) for x in w.inputs(s))
         fv.quantize_qkv(q, k, v, cal, "dynamic")
-    ring = np.float32(fv.state_read(cal)["ring"])
-    vals = (np.float32(margin) * ring.max(axis=1)).astype(np.float32)
+    vals = fv.calibrated_values(cal, margin)
     layer = "visual.blocks.0.attn.attn"
-    with tempfile.NamedTemporaryFile("w", suffix=".json", delete=False) as f:
-        json.dump({layer: {"q": float(vals[0]), "k": float(vals[1]), "v": float(vals[2])}}, f)
-        path = f.name
-    loaded = fv.load_static_scales(path, layer)
-    os.unlink(path)
-    assert np.array_equal(np.float32(loaded), vals)
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "scales.json")
+        fv.save_static_scales(path, layer, vals)
+        loaded = fv.load_static_scales(path, layer)
+    assert tuple(loaded) == tuple(vals)
     return [float(x) for x in loaded]
 
 

@@ -20,7 +20,8 @@ import torch
 __all__ = [
     "LIB_PATH", "FP8VIT_DYNAMIC", "FP8VIT_STATIC", "Fp8VitError",
     "state_bytes", "new_state", "state_init", "state_set_static", "scales_update",
-    "quantize_qkv", "attn_varlen", "attn_varlen_fp8out", "state_read", "load_static_scales", "status_str",
+    "quantize_qkv", "attn_varlen", "attn_varlen_fp8out", "state_read", "state_write", "calibrated_values",
+    "load_static_scales", "save_static_scales", "status_str",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8vit.so")
@@ -48,6 +49,9 @@ _SIGS = {
     "fp8vit_attn_varlen_fp8out": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
                                                  _vp, _vp, _i64, _vp]),
     "fp8vit_state_read": (ctypes.c_int, [_vp, ctypes.POINTER(_StateView), _vp]),
+    "fp8vit_state_write": (ctypes.c_int, [_vp, ctypes.POINTER(_StateView), _vp]),
+    "fp8vit_calibrated_values": (ctypes.c_int, [_vp, _f32, ctypes.POINTER(_f32), _vp]),
+    "fp8vit_save_static_scales": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_char_p, ctypes.POINTER(_f32)]),
     "fp8vit_status_str": (ctypes.c_char_p, [ctypes.c_int]),
 }
 _LIB = None
@@ -198,6 +202,34 @@ def state_read(state: torch.Tensor) -> dict:
         "amax_last": list(view.amax_last),
         "flags": int(view.flags),
     }
+
+
+def state_write(state: torch.Tensor, snapshot: dict) -> None:
+    """Restore a state from a dict shaped like state_read's result (synchronous)."""
+    view = _StateView()
+    for x in range(3):
+        for i in range(16):
+            view.ring[x][i] = float(snapshot["ring"][x][i])
+        view.static_values[x] = float(snapshot["static_values"][x])
+        view.descale_used[x] = float(snapshot["descale_used"][x])
+        view.amax_last[x] = float(snapshot["amax_last"][x])
+    view.count = int(snapshot["count"])
+    view.flags = int(snapshot.get("flags", 0))
+    _check("fp8vit_state_write", _lib.fp8vit_state_write(_ptr(state), ctypes.byref(view), _stream(state.device)))
+
+
+def calibrated_values(state: torch.Tensor, margin: float = 1.5) -> Tuple[float, float, float]:
+    """fp32(margin x ring window max) per tensor, as a calibration saves them."""
+    arr = (_f32 * 3)()
+    _check("fp8vit_calibrated_values",
+           _lib.fp8vit_calibrated_values(_ptr(state), float(margin), arr, _stream(state.device)))
+    return (arr[0], arr[1], arr[2])
+
+
+def save_static_scales(json_path: str, layer_name: str, values_qkv: Sequence[float]) -> None:
+    arr = (_f32 * 3)(*[float(x) for x in values_qkv])
+    _check("fp8vit_save_static_scales",
+           _lib.fp8vit_save_static_scales(os.fsencode(json_path), layer_name.encode("utf-8"), arr))
 
 
 def load_static_scales(json_path: str, layer_name: str) -> Tuple[float, float, float]:

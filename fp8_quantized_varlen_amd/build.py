@@ -17,7 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp8vit.so")
 
-HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.environ.get("HIPCC", f"{ROCM}/bin/hipcc")
 ARCH = "gfx950"
 # Packed fp32 VALU ops are kept out of generated code on purpose.
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{CSRC}",
@@ -31,7 +32,8 @@ def _compile(src: str) -> str:
     if src.endswith(".hip"):
         cmd = [HIPCC, f"--offload-arch={ARCH}", "-x", "hip", *COMMON, "-c", path, "-o", obj]
     else:
-        cmd = [HIPCC, *COMMON, "-c", path, "-o", obj]
+        # Host-only sources: no device pass.
+        cmd = [HIPCC, "-x", "c++", "-D__HIP_PLATFORM_AMD__=1", f"-I{ROCM}/include", *COMMON, "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

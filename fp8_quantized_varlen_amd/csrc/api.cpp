@@ -157,6 +157,52 @@ fp8vit_status fp8vit_state_read(const void* d_state, fp8vit_state_view* out, voi
   return FP8VIT_OK;
 }
 
+fp8vit_status fp8vit_state_write(void* d_state, const fp8vit_state_view* in, void* stream) {
+  if (!d_state || !in) return FP8VIT_ERR_INVALID_ARGUMENT;
+  if (!aligned(d_state, 256)) return FP8VIT_ERR_UNSUPPORTED;
+  auto nonneg = [](float x) { return std::isfinite(x) && x >= 0.0f; };
+  for (int x = 0; x < 3; ++x) {
+    for (int i = 0; i < FP8VIT_RING_SLOTS; ++i)
+      if (!nonneg(in->ring[x][i])) return FP8VIT_ERR_INVALID_ARGUMENT;
+    if (!nonneg(in->static_values[x]) || !nonneg(in->descale_used[x]) || !nonneg(in->amax_last[x]))
+      return FP8VIT_ERR_INVALID_ARGUMENT;
+  }
+  // The atomic-max scratch and the grid-barrier words start from zero, as
+  // after fp8vit_state_init.
+  DevState h;
+  std::memset(&h, 0, sizeof(h));
+  std::memcpy(h.ring, in->ring, sizeof(h.ring));
+  h.count = in->count;
+  for (int i = 0; i < 3; ++i) {
+    h.static_values[i] = in->static_values[i];
+    h.descale_used[i] = in->descale_used[i];
+    h.amax_last[i] = in->amax_last[i];
+  }
+  h.flags = in->flags;
+  hipError_t e = hipMemcpyAsync(d_state, &h, sizeof(DevState), hipMemcpyHostToDevice, as_stream(stream));
+  if (e != hipSuccess) return FP8VIT_ERR_HIP;
+  // `h` lives on this stack frame: wait for the copy before returning.
+  return from_hip(hipStreamSynchronize(as_stream(stream)));
+}
+
+fp8vit_status fp8vit_calibrated_values(const void* d_state, float margin, float out_qkv[3], void* stream) {
+  if (!d_state || !out_qkv) return FP8VIT_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(margin) || !(margin > 0.0f)) return FP8VIT_ERR_INVALID_ARGUMENT;
+  fp8vit_state_view v;
+  const fp8vit_status st = fp8vit_state_read(d_state, &v, stream);
+  if (st != FP8VIT_OK) return st;
+  float vals[3];
+  for (int x = 0; x < 3; ++x) {
+    float w = 0.0f;
+    for (int i = 0; i < FP8VIT_RING_SLOTS; ++i) w = v.ring[x][i] > w ? v.ring[x][i] : w;
+    vals[x] = margin * w;  // one fp32 product
+    if (!(vals[x] > 0.0f)) return FP8VIT_ERR_NOT_FOUND;
+    if (!std::isfinite(vals[x])) return FP8VIT_ERR_INVALID_ARGUMENT;
+  }
+  for (int i = 0; i < 3; ++i) out_qkv[i] = vals[i];
+  return FP8VIT_OK;
+}
+
 const char* fp8vit_status_str(fp8vit_status status) {
   switch (status) {
     case FP8VIT_OK: return "ok";

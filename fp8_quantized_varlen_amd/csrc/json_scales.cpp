@@ -5,6 +5,10 @@
 // "visual.blocks.0.attn.attn" to objects {"q": .., "k": .., "v": ..}; the keys
 // "q_scale", "k_scale", "v_scale" are accepted as aliases. The values already
 // include the calibration margin (Calibrate-Once Reuse Workflow section).
+//
+// The writer closes the calibrate-once loop in the library: it stores one
+// layer's calibrated values in such a file, keeping every other entry.
+#include <cerrno>
 #include <clocale>
 #include <cmath>
 #include <cstdio>
@@ -14,15 +18,22 @@
 #include <map>
 #include <memory>
 #include <string>
+#include <unistd.h>
 #include <vector>
 
 #include "fp8vit.h"
 
 namespace {
 
+locale_t c_locale() {
+  static locale_t c_loc = newlocale(LC_NUMERIC_MASK, "C", (locale_t)0);
+  return c_loc;
+}
+
 struct JValue {
   enum Kind { Null, Bool, Number, String, Array, Object } kind = Null;
   double num = 0.0;
+  std::string raw;  // a number's text as it was read
   bool b = false;
   std::string str;
   std::vector<JValue> arr;
@@ -125,7 +136,7 @@ class Parser {
     }
     return false;
   }
-  bool number(double& v) {
+  bool number(double& v, std::string& raw) {
     const char* start = p_;
     if (p_ < e_ && *p_ == '-') ++p_;
     if (p_ >= e_) return false;
@@ -148,8 +159,9 @@ class Parser {
       while (p_ < e_ && *p_ >= '0' && *p_ <= '9') ++p_;
     }
     std::string tok(start, p_);
+    raw = tok;
     // strtod in the "C" locale: the grammar above already fixed the syntax.
-    static locale_t c_loc = newlocale(LC_NUMERIC_MASK, "C", (locale_t)0);
+    const locale_t c_loc = c_locale();
     char* end = nullptr;
     v = c_loc ? strtod_l(tok.c_str(), &end, c_loc) : strtod(tok.c_str(), &end);
     return end && *end == '\0';
@@ -200,7 +212,7 @@ class Parser {
     if (c == 'f') { out.kind = JValue::Bool; out.b = false; return lit("false"); }
     if (c == 'n') { out.kind = JValue::Null; return lit("null"); }
     out.kind = JValue::Number;
-    return number(out.num);
+    return number(out.num, out.raw);
   }
 };
 
@@ -211,24 +223,105 @@ const JValue* find_last(const JValue& obj, const char* key) {
   return r;
 }
 
-}  // namespace
-
-extern "C" fp8vit_status fp8vit_load_static_scales(const char* json_path, const char* layer_name,
-                                                   float out_qkv[3]) {
-  if (!json_path || !layer_name || !out_qkv) return FP8VIT_ERR_INVALID_ARGUMENT;
-  FILE* f = fopen(json_path, "rb");
-  if (!f) return FP8VIT_ERR_IO;
-  std::string buf;
+// Whole file into `buf`; false with errno kept when it cannot be opened or read.
+bool read_file(const char* path, std::string& buf) {
+  FILE* f = fopen(path, "rb");
+  if (!f) return false;
   char tmp[65536];
   size_t n;
   while ((n = fread(tmp, 1, sizeof(tmp), f)) > 0) buf.append(tmp, n);
   const bool err = ferror(f) != 0;
   fclose(f);
-  if (err) return FP8VIT_ERR_IO;
+  return !err;
+}
+
+const char* skip_bom(const std::string& buf) {
   const char* b = buf.data();
-  const char* e = b + buf.size();
   if (buf.size() >= 3 && (unsigned char)b[0] == 0xEF && (unsigned char)b[1] == 0xBB && (unsigned char)b[2] == 0xBF)
-    b += 3;  // UTF-8 byte order mark
+    b += 3;
+  return b;
+}
+
+// ---- writer ----------------------------------------------------------------
+
+// Shortest "%.{p}g" text of a float that reads back (strtod, then rounding to
+// float, as the loader reads it) to the same value; p <= 9 always suffices.
+// Formatting and parsing both run in the "C" locale, whatever the caller's
+// locale is.
+std::string format_float(float v) {
+  locale_t loc = c_locale();
+  locale_t old = loc ? uselocale(loc) : (locale_t)0;
+  char text[40];
+  for (int p = 1; p <= 9; ++p) {
+    snprintf(text, sizeof(text), "%.*g", p, (double)v);
+    char* end = nullptr;
+    const double back = loc ? strtod_l(text, &end, loc) : strtod(text, &end);
+    if ((float)back == v) break;
+  }
+  if (old) uselocale(old);
+  return text;
+}
+
+void write_string(std::string& o, const std::string& s) {
+  o.push_back('"');
+  for (unsigned char c : s) {
+    if (c == '"') o += "\\\"";
+    else if (c == '\\') o += "\\\\";
+    else if (c < 0x20) {
+      char esc[8];
+      snprintf(esc, sizeof(esc), "\\u%04x", (unsigned)c);
+      o += esc;
+    } else {
+      o.push_back((char)c);
+    }
+  }
+  o.push_back('"');
+}
+
+// Compact serialization; object keys keep their order (duplicates included)
+// and numbers their text as read.
+void write_value(std::string& o, const JValue& v) {
+  switch (v.kind) {
+    case JValue::Null: o += "null"; break;
+    case JValue::Bool: o += v.b ? "true" : "false"; break;
+    case JValue::Number: o += v.raw; break;
+    case JValue::String: write_string(o, v.str); break;
+    case JValue::Array:
+      o.push_back('[');
+      for (size_t i = 0; i < v.arr.size(); ++i) {
+        if (i) o += ", ";
+        write_value(o, v.arr[i]);
+      }
+      o.push_back(']');
+      break;
+    case JValue::Object:
+      o.push_back('{');
+      for (size_t i = 0; i < v.obj.size(); ++i) {
+        if (i) o += ", ";
+        write_string(o, v.obj[i].first);
+        o += ": ";
+        write_value(o, v.obj[i].second);
+      }
+      o.push_back('}');
+      break;
+  }
+}
+
+bool only_whitespace(const char* b, const char* e) {
+  for (; b < e; ++b)
+    if (!(*b == ' ' || *b == '\t' || *b == '\n' || *b == '\r')) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" fp8vit_status fp8vit_load_static_scales(const char* json_path, const char* layer_name,
+                                                   float out_qkv[3]) {
+  if (!json_path || !layer_name || !out_qkv) return FP8VIT_ERR_INVALID_ARGUMENT;
+  std::string buf;
+  if (!read_file(json_path, buf)) return FP8VIT_ERR_IO;
+  const char* b = skip_bom(buf);  // UTF-8 byte order mark
+  const char* e = buf.data() + buf.size();
   JValue root;
   Parser p(b, e);
   if (!p.parse_document(root) || root.kind != JValue::Object) return FP8VIT_ERR_PARSE;
@@ -250,5 +343,68 @@ extern "C" fp8vit_status fp8vit_load_static_scales(const char* json_path, const 
     vals[i] = fv;
   }
   for (int i = 0; i < 3; ++i) out_qkv[i] = vals[i];
+  return FP8VIT_OK;
+}
+
+extern "C" fp8vit_status fp8vit_save_static_scales(const char* json_path, const char* layer_name,
+                                                   const float values_qkv[3]) {
+  if (!json_path || !layer_name || !values_qkv) return FP8VIT_ERR_INVALID_ARGUMENT;
+  for (int i = 0; i < 3; ++i)
+    if (!std::isfinite(values_qkv[i]) || !(values_qkv[i] > 0.0f)) return FP8VIT_ERR_INVALID_ARGUMENT;
+
+  // Existing entries are kept; a missing file starts an empty object.
+  JValue root;
+  root.kind = JValue::Object;
+  std::string buf;
+  if (read_file(json_path, buf)) {
+    const char* b = skip_bom(buf);
+    const char* e = buf.data() + buf.size();
+    if (!only_whitespace(b, e)) {
+      Parser p(b, e);
+      if (!p.parse_document(root) || root.kind != JValue::Object) return FP8VIT_ERR_PARSE;
+    }
+  } else if (errno != ENOENT) {
+    return FP8VIT_ERR_IO;
+  }
+
+  std::string entry = "{\"q\": " + format_float(values_qkv[0]) + ", \"k\": " +
+                      format_float(values_qkv[1]) + ", \"v\": " + format_float(values_qkv[2]) + "}";
+  // One top-level entry per line; the layer replaces its first occurrence (and
+  // drops later duplicates), or is appended.
+  std::string out = "{";
+  bool placed = false, first = true;
+  auto line = [&](const std::string& key, const std::string& val) {
+    out += first ? "\n  " : ",\n  ";
+    first = false;
+    write_string(out, key);
+    out += ": ";
+    out += val;
+  };
+  for (const auto& kv : root.obj) {
+    if (kv.first == layer_name) {
+      if (!placed) line(kv.first, entry);
+      placed = true;
+      continue;
+    }
+    std::string val;
+    write_value(val, kv.second);
+    line(kv.first, val);
+  }
+  if (!placed) line(layer_name, entry);
+  out += first ? "}\n" : "\n}\n";
+
+  // Write a sibling file, then rename it over the target: readers see the old
+  // or the new file, never a partial one.
+  const std::string tmp = std::string(json_path) + ".tmp." + std::to_string((long)getpid());
+  FILE* f = fopen(tmp.c_str(), "wb");
+  if (!f) return FP8VIT_ERR_IO;
+  bool ok = fwrite(out.data(), 1, out.size(), f) == out.size();
+  ok = (fflush(f) == 0) && ok;
+  ok = (fclose(f) == 0) && ok;
+  if (ok) ok = rename(tmp.c_str(), json_path) == 0;
+  if (!ok) {
+    remove(tmp.c_str());
+    return FP8VIT_ERR_IO;
+  }
   return FP8VIT_OK;
 }

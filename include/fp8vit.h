@@ -178,6 +178,43 @@ fp8vit_status fp8vit_attn_varlen_fp8out(const void* q8, const void* k8, const vo
  * `stream`, then waits for it). Not for the hot path. */
 fp8vit_status fp8vit_state_read(const void* d_state, fp8vit_state_view* out, void* stream);
 
+/* Synchronous write of a whole state, the inverse of fp8vit_state_read: ring,
+ * count, static values, last descales, last amax and flags are taken from
+ * `in`; the internal atomic-max scratch and barrier words are cleared as by
+ * fp8vit_state_init. With it a calibration or a dynamic ring can be saved and
+ * resumed: the forwards that follow behave as they would have in the process
+ * that read the state. Ring, static, descale and amax entries must be finite
+ * and >= 0 (else ERR_INVALID_ARGUMENT). Copies on `stream` and waits for it,
+ * so it is not for graph capture. */
+fp8vit_status fp8vit_state_write(void* d_state, const fp8vit_state_view* in, void* stream);
+
+/* Synchronous. The values a calibration saves (vLLM page "FP8 ViT Encoder
+ * Attention", Calibrate-Once Reuse Workflow: dynamic scaling over the
+ * calibration passes, then the learned values times a margin, default 1.5):
+ * out_qkv[i] = fp32(margin * W_i), one fp32 product, where W_i is the maximum
+ * over the 16 ring slots of tensor i. Errors: ERR_INVALID_ARGUMENT (null
+ * pointer, margin not finite or <= 0, a product that overflows),
+ * ERR_NOT_FOUND (a tensor whose ring holds no amax > 0: no dynamic forward has
+ * been recorded, or every input was zero), ERR_HIP. out_qkv is written only on
+ * FP8VIT_OK. */
+fp8vit_status fp8vit_calibrated_values(const void* d_state, float margin, float out_qkv[3], void* stream);
+
+/* Host only. Store one layer's static q/k/v values in the JSON scale file at
+ * `json_path` (vLLM page, Scale File Format and Calibrate-Once Reuse Workflow:
+ * the file maps layer names to {"q", "k", "v"} values that already include the
+ * margin), so that fp8vit_load_static_scales reads back exactly these floats.
+ * An existing file keeps its other entries (in order, numbers as written,
+ * strings re-escaped, whitespace normalised); an entry named
+ * `layer_name` is replaced in place (later duplicates of it are dropped), or
+ * appended. A missing or whitespace-only file starts an empty object. The new
+ * file is written beside the target and renamed over it. Values are written
+ * as the shortest decimal that reads back to the same float. Errors:
+ * ERR_INVALID_ARGUMENT (null argument; a value that is not finite and > 0),
+ * ERR_PARSE (the existing file is not a JSON object: it is left untouched),
+ * ERR_IO (cannot read the existing file, or cannot write or rename). */
+fp8vit_status fp8vit_save_static_scales(const char* json_path, const char* layer_name,
+                                        const float values_qkv[3]);
+
 /* Static string naming a status code. */
 const char* fp8vit_status_str(fp8vit_status status);
 

@@ -29,7 +29,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 10, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -86,6 +86,25 @@ def test_argument_validation_before_any_hip_call(lib):
     lib.fp8vit_state_init.argtypes = [vp, vp]
     assert lib.fp8vit_state_init(null, null) == 1
     assert lib.fp8vit_state_init(vp(0x10010), null) == 2
+    c = lib.fp8vit_calibrated_values
+    c.argtypes = [vp, ctypes.c_float, ctypes.POINTER(ctypes.c_float), vp]
+    out = (ctypes.c_float * 3)()
+    assert c(null, 1.5, out, null) == 1
+    for bad in (0.0, -1.5, float("nan"), float("inf")):
+        assert c(fake, bad, out, null) == 1
+    assert c(vp(0x10010), 1.5, out, null) == 2
+    from fp8_quantized_varlen_amd import _StateView
+    w = lib.fp8vit_state_write
+    w.argtypes = [vp, vp, vp]
+    view = _StateView()
+    assert w(fake, null, null) == 1 and w(null, ctypes.addressof(view), null) == 1
+    assert w(vp(0x10010), ctypes.addressof(view), null) == 2
+    for field, i, bad in (("ring", 0, -1.0), ("ring", 5, float("nan")), ("ring", 15, float("inf")),
+                          ("static_values", 0, -0.5), ("descale_used", 1, -2.0), ("amax_last", 2, float("inf"))):
+        arr = getattr(view, field) if field != "ring" else view.ring[2]
+        arr[i] = bad
+        assert w(fake, ctypes.addressof(view), null) == 1, (field, i)
+        arr[i] = 0.0
 
 
 def load(lib, path, layer):
