@@ -39,8 +39,9 @@ PAGE_MI300X_TFLOPS = {"l8192_hd72_static": 4 * 16 * 72 * 8192 ** 2 / 2.364e-3 / 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=100,
+                   help="untimed steps first; the GPU clock needs some tens of ms of load to settle")
     p.add_argument("--workload", default="l8192_hd72_static")
     p.add_argument("--rotate-mb", type=float, default=600.0,
                    help="cycle through input copies totalling at least this many MB (defeats the 256 MB MALL)")
@@ -50,6 +51,8 @@ def parse():
                    help="q,k,v static values to use instead of calibrating (profiling runs: no dynamic passes)")
     p.add_argument("--out", choices=("bf16", "fp8"), default="bf16",
                    help="attention output: bf16, or e4m3 with a static output descale (fused fp8 output)")
+    p.add_argument("--graph", action="store_true",
+                   help="also time the steps as one captured HIP graph (no host launch gaps)")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 256 MiB device copy (for scaling HBM byte counters)")
     return p.parse_args()
@@ -153,9 +156,20 @@ def cpu_baseline(w, qb, kb, vb, static_values, out_gpu, target_s, compare=True):
                 "seconds_per_step": round(step_s, 3)}
     vmax = float(np.abs(oracle.quant.bf16_to_f32(vb)).max())
     err = max(float(np.abs(out_gpu[a:a + n, h].astype(np.float64) - o).max()) for a, _, n, h, o in rows_out)
+    # the method's own error on the same rows: unquantized fp64 attention of the bf16 inputs
+    fp = [oracle.quant.bf16_to_f32(x) for x in (qb, kb, vb)]
+    e_gpu = e_orc = ref2 = 0.0
+    for a, b, n, h, o in rows_out:
+        r = oracle.attention._segment_head(*(np.asarray(x, np.float64) for x in
+                                             (fp[0][a:a + n, h], fp[1][a:b, h], fp[2][a:b, h])), sigma)
+        e_gpu += float(np.sum((out_gpu[a:a + n, h].astype(np.float64) - r) ** 2))
+        e_orc += float(np.sum((o - r) ** 2))
+        ref2 += float(np.sum(r ** 2))
     return {"value": value, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle", "sample": sample,
             "seconds_per_step": round(step_s, 3),
             "gpu_vs_oracle_max_abs_over_vmax": err / vmax if vmax > 0 else 0.0,
+            "gpu_rel_rms_vs_fp64": (e_gpu / ref2) ** 0.5 if ref2 > 0 else 0.0,
+            "oracle_rel_rms_vs_fp64": (e_orc / ref2) ** 0.5 if ref2 > 0 else 0.0,
             "gpu_rows_checked": int(sum(n for _, _, n, _, _ in rows_out))}
 
 
@@ -253,6 +267,27 @@ def main():
     quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
 
+    graph_ms = None
+    if args.graph:
+        # the same steps captured once and replayed: device time without launch gaps
+        gs = torch.cuda.Stream()
+        gs.wait_stream(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gs):
+            for i in range(args.steps):
+                step(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        gstart, gend = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gstart.record()
+        g.replay()
+        gend.record()
+        torch.cuda.synchronize()
+        graph_ms = gstart.elapsed_time(gend) / args.steps
+        del g
+
     if args.calib_copy:
         a = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -292,6 +327,8 @@ def main():
                      "traffic": attn_traffic(w.name, d),
                      "kernel": "attn_kernel<%d>" % d},
         "descale_used": state["descale_used"],
+        **({"graph": {"ms_per_step": round(graph_ms, 4),
+                      "value": round(w.flops / (graph_ms * 1e-3) / 1e12, 2)}} if graph_ms else {}),
         "wall_s_timed_region": round(t_wall, 3),
     }
     if not args.no_cpu_baseline:

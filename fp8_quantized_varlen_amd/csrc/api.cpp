@@ -167,7 +167,7 @@ fp8vit_status fp8vit_state_write(void* d_state, const fp8vit_state_view* in, voi
     if (!nonneg(in->static_values[x]) || !nonneg(in->descale_used[x]) || !nonneg(in->amax_last[x]))
       return FP8VIT_ERR_INVALID_ARGUMENT;
   }
-  // The atomic-max scratch and the grid-barrier words start from zero, as
+  // The atomic-max scratch and the arrival counter start from zero, as
   // after fp8vit_state_init.
   DevState h;
   std::memset(&h, 0, sizeof(h));

@@ -16,18 +16,17 @@ struct alignas(256) DevState {
   float static_values[3];            // static q/k/v values (margin included)
   float descale_used[3];             // descales of the last quantize / update
   float amax_last[3];                // amax of the last dynamic forward
-  uint32_t flags;                    // bit 0: grid barrier gave up waiting
+  uint32_t flags;                    // reserved: 0
   uint32_t reserved0;
-  uint32_t amax_bits[2][4];          // atomicMax scratch, double-buffered by count parity
-  uint32_t bar_arrived;              // grid barrier: blocks arrived in this round
-  uint32_t bar_generation;           // grid barrier: completed rounds
+  uint32_t amax_bits[2][4];          // atomic-max scratch of the amax pass (row 0); 0 between forwards
+  uint32_t bar_arrived;              // blocks of the amax pass that finished; 0 between forwards
+  uint32_t reserved2;
   uint32_t reserved1[54];
 };
 static_assert(sizeof(DevState) == 512, "state layout");
 
 constexpr float kFp8Max = 448.0f;
 constexpr float kDescaleFloor = 1e-10f;
-constexpr uint32_t kFlagBarrierTimeout = 1u;
 
 // Launch wrappers (defined in the .hip files). All return hipError_t of the launch.
 hipError_t launch_state_init(DevState* st, hipStream_t s);

@@ -1,4 +1,5 @@
-// Fused per-tensor e4m3 quantization of Q, K and V in one launch.
+// Per-tensor e4m3 quantization of Q, K and V: one launch in static mode, two
+// in dynamic mode.
 //
 // Per element (atrex-bench #025 per_token_group_quant_fp8, Reference
 // Implementation, with one group per tensor): y = x / descale as an IEEE fp32
@@ -16,11 +17,13 @@
 //
 // Dynamic mode (vLLM page "FP8 ViT Encoder Attention", Usage): the amax of
 // each whole tensor is reduced first, pushed into the 16-slot ring, and the
-// window maximum sets this forward's descale. The amax pass and the quantize
-// pass share one cooperative launch separated by a grid-wide barrier, so the
-// three tensors cost a single launch instead of a reduction launch plus three
-// quantization launches (the same page names "3 quantization kernel launches"
-// as the small-image overhead).
+// window maximum sets this forward's descale. Two launches: the amax pass
+// (whose last block to finish does the ring bookkeeping) and the quantize
+// pass, which reads the descales from the state. A single cooperative launch
+// with a grid-wide barrier between the passes reads the input once, but on
+// MI355X it measured slower at every size: the cooperative launch itself adds
+// ~17 us and a barrier across eight XCDs costs several device-scope atomic
+// round trips, against ~7 us for re-reading 57 MB (L = 8192, 16 heads, d = 72).
 //
 // Data layout: bf16 rows of H*d elements with token stride ld; every thread
 // moves 16-byte chunks (8 elements) in and 8-byte chunks out, consecutive
@@ -32,17 +35,8 @@ namespace fp8vit {
 
 constexpr int kQuantThreads = 512;
 constexpr int kUnroll = 4;   // chunks per tensor in flight per thread (12 for the three)
-// Dynamic mode: one block of 1024 threads per CU. When every thread's share
-// is at most kResident chunks per tensor (up to 8M elements per tensor on 256
-// CUs), the chunks loaded for the amax stay in registers across the grid
-// barrier and are quantized from there: the input is read once.
-constexpr int kDynThreads = 1024;
-constexpr int kResident = 8;
-// Upper bound on one grid-barrier wait, in ticks of the 100 MHz real-time
-// counter (20 ms). Reaching it means the co-residency assumption failed; the
-// state flag records it and the kernel still runs to completion.
-constexpr uint64_t kBarrierTimeoutTicks = 2000000ull;
-
+constexpr int kAmaxBlocks = 128;
+constexpr int kAmaxUnroll = 4;
 __device__ __forceinline__ uint32_t bf16_lo(uint32_t w) { return w << 16; }
 __device__ __forceinline__ uint32_t bf16_hi(uint32_t w) { return w & 0xffff0000u; }
 
@@ -110,24 +104,24 @@ __device__ __forceinline__ void quantize_all(const QuantArgs& a, uint32_t n8, co
 }
 
 // Largest |x| bits of each of Q, K, V over this thread's chunks (the same
-// chunks quantize_all visits), with 3 * kUnroll loads in flight.
+// chunk pattern as quantize_all), with 3 * kAmaxUnroll loads in flight.
 template <bool CONTIG>
 __device__ __forceinline__ void absmax_all(const QuantArgs& a, uint32_t n8, uint32_t gtid, uint32_t gstride,
                                            uint32_t m[3]) {
   m[0] = m[1] = m[2] = 0;
-  for (uint32_t base = gtid; base < n8; base += gstride * kUnroll) {
-    uint4 w[3][kUnroll];
+  for (uint32_t base = gtid; base < n8; base += gstride * kAmaxUnroll) {
+    uint4 w[3][kAmaxUnroll];
 #pragma unroll
     for (int x = 0; x < 3; ++x)
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < kAmaxUnroll; ++u) {
         const uint32_t c = base + u * gstride;
         w[x][u] = c < n8 ? *chunk_src<CONTIG>(a.x[x], a.ld[x], a.row8, c) : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
     for (int x = 0; x < 3; ++x)
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) m[x] = max(m[x], chunk_absmax_bits(w[x][u]));
+      for (int u = 0; u < kAmaxUnroll; ++u) m[x] = max(m[x], chunk_absmax_bits(w[x][u]));
   }
 }
 
@@ -145,34 +139,11 @@ __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* red) {
   return r;
 }
 
-// Sense-free generation barrier over all blocks of a cooperative launch. The
-// wait is bounded: on timeout the state's flag is raised and the block goes on,
-// so every wave always exits.
-__device__ void grid_barrier(DevState* st, uint32_t nblocks) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t gen = __hip_atomic_load(&st->bar_generation, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-    uint32_t prev = __hip_atomic_fetch_add(&st->bar_arrived, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (prev + 1 == nblocks) {
-      __hip_atomic_store(&st->bar_arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_add(&st->bar_generation, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      while (__hip_atomic_load(&st->bar_generation, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
-        __builtin_amdgcn_s_sleep(8);
-        if (__builtin_amdgcn_s_memrealtime() - t0 > kBarrierTimeoutTicks) {
-          __hip_atomic_fetch_or(&st->flags, kFlagBarrierTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-      }
-      __atomic_thread_fence(__ATOMIC_ACQUIRE);
-    }
-  }
-  __syncthreads();
-}
-
-template <bool CONTIG>
-__global__ __launch_bounds__(kQuantThreads) void quant_static_kernel(QuantArgs a) {
+// Quantize pass. Static mode: the descales come from the stored static
+// values (block 0 records them). Dynamic mode: the amax pass already wrote
+// them to the state.
+template <bool CONTIG, bool DYNAMIC>
+__global__ __launch_bounds__(kQuantThreads) void quant_kernel(QuantArgs a) {
   __shared__ double rcp[3];
   const uint32_t gtid = blockIdx.x * kQuantThreads + threadIdx.x;
   const uint32_t gstride = gridDim.x * kQuantThreads;
@@ -180,9 +151,9 @@ __global__ __launch_bounds__(kQuantThreads) void quant_static_kernel(QuantArgs a
   if (threadIdx.x == 0) {
 #pragma unroll
     for (int x = 0; x < 3; ++x) {
-      const float d = descale_from_amax(a.st->static_values[x]);
+      const float d = DYNAMIC ? a.st->descale_used[x] : descale_from_amax(a.st->static_values[x]);
       rcp[x] = 1.0 / (double)d;
-      if (blockIdx.x == 0) a.st->descale_used[x] = d;
+      if (!DYNAMIC && blockIdx.x == 0) a.st->descale_used[x] = d;
     }
   }
   __syncthreads();
@@ -190,149 +161,93 @@ __global__ __launch_bounds__(kQuantThreads) void quant_static_kernel(QuantArgs a
   quantize_all<CONTIG>(a, n8, r, gtid, gstride);
 }
 
+// Amax pass of dynamic mode. Each block reduces its chunks of Q, K and V and
+// atomic-maxes the three results into the state's scratch; then it arrives at
+// a counter. The block that arrives last sees every other block's maxima
+// (each arrival is a release, the last one an acquire), pushes the triple
+// into ring slot count % 16, writes the descales from the window maximum
+// including it, and clears the scratch and the counter for the next forward.
 template <bool CONTIG>
-__global__ __launch_bounds__(kDynThreads) void quant_dynamic_kernel(QuantArgs a) {
-  __shared__ uint32_t red[kDynThreads / 64];
-  __shared__ double rcp[3];
-  const uint32_t gtid = blockIdx.x * kDynThreads + threadIdx.x;
-  const uint32_t gstride = gridDim.x * kDynThreads;
+__global__ __launch_bounds__(kQuantThreads) void amax_kernel(QuantArgs a) {
+  __shared__ uint32_t red[kQuantThreads / 64];
+  __shared__ uint32_t is_last;
+  const uint32_t gtid = blockIdx.x * kQuantThreads + threadIdx.x;
+  const uint32_t gstride = gridDim.x * kQuantThreads;
   const uint32_t n8 = (uint32_t)a.T * (uint32_t)a.row8;
-  const bool resident = n8 <= gstride * (uint32_t)kResident;   // grid-uniform
   DevState* st = a.st;
-  // Ring and count are read before the barrier; block 0 rewrites them after it.
-  const uint32_t count = st->count;
-  const uint32_t par = count & 1u;
-  float ring_max_other[3];
-  {
-    const uint32_t slot = count % FP8VIT_RING_SLOTS;
-#pragma unroll
-    for (int x = 0; x < 3; ++x) {
-      float w = 0.0f;
-#pragma unroll
-      for (int i = 0; i < FP8VIT_RING_SLOTS; ++i) {
-        float r = st->ring[x][i];
-        w = (i != (int)slot && r > w) ? r : w;
-      }
-      ring_max_other[x] = w;
-    }
-  }
-  // Phase A: amax of each tensor.
-  uint4 held[3][kResident];
-  uint32_t mt[3] = {0, 0, 0};
-  if (resident) {
-#pragma unroll
-    for (int x = 0; x < 3; ++x)
-#pragma unroll
-      for (int u = 0; u < kResident; ++u) {
-        const uint32_t c = gtid + u * gstride;
-        held[x][u] = c < n8 ? *chunk_src<CONTIG>(a.x[x], a.ld[x], a.row8, c) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-    for (int x = 0; x < 3; ++x)
-#pragma unroll
-      for (int u = 0; u < kResident; ++u) mt[x] = max(mt[x], chunk_absmax_bits(held[x][u]));
-  } else {
-    absmax_all<CONTIG>(a, n8, gtid, gstride, mt);
-  }
+  uint32_t mt[3];
+  absmax_all<CONTIG>(a, n8, gtid, gstride, mt);
 #pragma unroll
   for (int x = 0; x < 3; ++x) {
-    const uint32_t m = block_max<kDynThreads>(mt[x], red);
+    const uint32_t m = block_max<kQuantThreads>(mt[x], red);
     if (threadIdx.x == 0 && m != 0u)
-      __hip_atomic_fetch_max(&st->amax_bits[par][x], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_max(&st->amax_bits[0][x], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  grid_barrier(st, gridDim.x);
-  // Phase B: descales from the window max including this forward (one
-  // thread per block; the reciprocals go to the block through LDS).
   if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(&st->bar_arrived, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = prev + 1 == gridDim.x;
+  }
+  __syncthreads();
+  if (is_last && threadIdx.x == 0) {
     float amax[3], d[3];
 #pragma unroll
     for (int x = 0; x < 3; ++x) {
-      uint32_t bits = __hip_atomic_load(&st->amax_bits[par][x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t bits = __hip_atomic_load(&st->amax_bits[0][x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       amax[x] = __uint_as_float(bits << 16);
-      float w = amax[x] > ring_max_other[x] ? amax[x] : ring_max_other[x];
-      d[x] = descale_from_amax(w);
-      rcp[x] = 1.0 / (double)d[x];
     }
-    if (blockIdx.x == 0) {
-      ring_commit(st, count, amax, d);
-#pragma unroll
-      for (int x = 0; x < 3; ++x) st->amax_bits[par ^ 1u][x] = 0u;   // scratch of the next forward
-    }
-  }
-  __syncthreads();
-  // Phase C: quantize.
-  const double r[3] = {rcp[0], rcp[1], rcp[2]};
-  if (resident) {
+    const uint32_t count = st->count;
+    ring_window_descales(st, count, amax, d);
+    ring_commit(st, count, amax, d);
 #pragma unroll
     for (int x = 0; x < 3; ++x)
-#pragma unroll
-      for (int u = 0; u < kResident; ++u) {
-        const uint32_t c = gtid + u * gstride;
-        if (c < n8) reinterpret_cast<uint2*>(a.y[x])[c] = quant_chunk(held[x][u], r[x]);
-      }
-  } else {
-    quantize_all<CONTIG>(a, n8, r, gtid, gstride);
+      __hip_atomic_store(&st->amax_bits[0][x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&st->bar_arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 namespace {
-struct DeviceInfo {
-  int cus = 0;
-  int coop_blocks_contig = 0;
-  int coop_blocks_strided = 0;
-};
-DeviceInfo g_info[64];
+int g_cus[64];
 
-const DeviceInfo& device_info() {
+int device_cus() {
   int dev = 0;
   (void)hipGetDevice(&dev);
-  DeviceInfo& di = g_info[dev & 63];
-  if (di.cus == 0) {
-    hipDeviceProp_t p;
-    if (hipGetDeviceProperties(&p, dev) == hipSuccess) {
-      int b1 = 0, b2 = 0;
-      (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&b1, quant_dynamic_kernel<true>, kDynThreads, 0);
-      (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&b2, quant_dynamic_kernel<false>, kDynThreads, 0);
-      di.coop_blocks_contig = (b1 > 0 ? b1 : 1) * p.multiProcessorCount;
-      di.coop_blocks_strided = (b2 > 0 ? b2 : 1) * p.multiProcessorCount;
-      di.cus = p.multiProcessorCount;
-    }
+  int& n = g_cus[dev & 63];
+  if (n == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) n = v;
   }
-  return di;
+  return n;
 }
 }  // namespace
 
 hipError_t launch_quantize(const QuantArgs& a, bool dynamic, hipStream_t s) {
-  const DeviceInfo& di = device_info();
-  if (di.cus == 0) return hipErrorInvalidDevice;
+  const int cus = device_cus();
+  if (cus == 0) return hipErrorInvalidDevice;
   const bool contig = a.ld[0] == 8LL * a.row8 && a.ld[1] == 8LL * a.row8 && a.ld[2] == 8LL * a.row8;
   const uint64_t n8 = (uint64_t)a.T * (uint64_t)a.row8;
-  const uint64_t want = (n8 + (uint64_t)kQuantThreads * kUnroll - 1) / ((uint64_t)kQuantThreads * kUnroll);
-  if (!dynamic) {
-    uint64_t g = want < 1 ? 1 : want;
-    const uint64_t cap = (uint64_t)di.cus * 4;
-    if (g > cap) g = cap;
-    if (contig)
-      hipLaunchKernelGGL(quant_static_kernel<true>, dim3((unsigned)g), dim3(kQuantThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL(quant_static_kernel<false>, dim3((unsigned)g), dim3(kQuantThreads), 0, s, a);
-    return hipGetLastError();
-  }
-  // At most one block per CU, all on the chip together while they wait at the
-  // grid barrier (the cooperative launch refuses grids that could not be);
-  // just enough blocks for the register-resident path when it applies.
-  const uint64_t per_block = (uint64_t)kDynThreads * kResident;
-  uint64_t g = (n8 + per_block - 1) / per_block;
+  uint64_t g = (n8 + (uint64_t)kQuantThreads * kUnroll - 1) / ((uint64_t)kQuantThreads * kUnroll);
   if (g < 1) g = 1;
-  uint64_t cap = (uint64_t)di.cus;
-  const uint64_t coresident = (uint64_t)(contig ? di.coop_blocks_contig : di.coop_blocks_strided);
-  if (cap > coresident) cap = coresident;
-  if (g > cap) g = cap;
-  QuantArgs args = a;
-  void* params[] = {&args};
-  const void* fn = contig ? reinterpret_cast<const void*>(quant_dynamic_kernel<true>)
-                          : reinterpret_cast<const void*>(quant_dynamic_kernel<false>);
-  return hipLaunchCooperativeKernel(fn, dim3((unsigned)g), dim3(kDynThreads), params, 0, s);
+  if (g > (uint64_t)cus * 4) g = (uint64_t)cus * 4;
+  const dim3 grid((unsigned)g), block(kQuantThreads);
+  if (dynamic) {
+    const dim3 agrid((unsigned)(g < (uint64_t)kAmaxBlocks ? g : (uint64_t)kAmaxBlocks));
+    if (contig)
+      hipLaunchKernelGGL(amax_kernel<true>, agrid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL(amax_kernel<false>, agrid, block, 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (contig)
+      hipLaunchKernelGGL((quant_kernel<true, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((quant_kernel<false, true>), grid, block, 0, s, a);
+  } else {
+    if (contig)
+      hipLaunchKernelGGL((quant_kernel<true, false>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((quant_kernel<false, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace fp8vit

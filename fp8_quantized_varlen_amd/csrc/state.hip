@@ -30,8 +30,7 @@ __global__ void scales_update_kernel(DevState* st, const float* amax) {
     float d[3];
     ring_window_descales(st, st->count, a, d);
     ring_commit(st, st->count, a, d);
-    // The fused quantizer keeps its amax scratch clean for the parity of the
-    // next count; a standalone update shifts the parity, so clear both.
+    // The amax pass leaves its scratch at zero; keep it so.
     for (int p = 0; p < 2; ++p)
       for (int x = 0; x < 4; ++x) st->amax_bits[p][x] = 0u;
   }

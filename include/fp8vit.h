@@ -63,7 +63,7 @@ typedef struct fp8vit_state_view {
   float static_values[3];           /* values given to fp8vit_state_set_static */
   float descale_used[3];            /* descales of the last quantize (or scales_update) */
   float amax_last[3];               /* amax observed by the last dynamic forward */
-  uint32_t flags;                   /* bit 0: a grid barrier gave up waiting (never expected) */
+  uint32_t flags;                   /* reserved: 0 */
 } fp8vit_state_view;
 
 /* Bytes of device memory one layer's state needs. The caller allocates it
@@ -103,14 +103,16 @@ fp8vit_status fp8vit_state_set_static(void* d_state, const float values_qkv[3], 
  * atrex-bench #025 for the division and the floor). One thread on `stream`. */
 fp8vit_status fp8vit_scales_update(void* d_state, const float* d_amax_qkv, void* stream);
 
-/* Quantize Q, K and V to e4m3 in one kernel launch.
+/* Quantize Q, K and V to e4m3: one kernel launch in static mode, two in
+ * dynamic mode.
  *   q, k, v      bf16 device tensors [total_tokens, num_heads, head_dim] with
  *                token strides ld_q, ld_k, ld_v (elements, >= H*d, multiples
  *                of 8); base pointers 16-byte aligned.
  *   mode         FP8VIT_DYNAMIC: amax of each whole tensor (all tokens, all
  *                heads) is pushed into the ring and the descale comes from the
- *                16-slot window max including this forward (one grid-wide
- *                barrier inside the launch). FP8VIT_STATIC: descale from the
+ *                16-slot window max including this forward (an amax pass,
+ *                whose last block does the ring bookkeeping, then the
+ *                quantize pass). FP8VIT_STATIC: descale from the
  *                stored static values; no amax pass, ring untouched.
  *   q8, k8, v8   uint8 e4m3fn outputs, contiguous [total_tokens, H, d],
  *                16-byte aligned.
@@ -180,7 +182,7 @@ fp8vit_status fp8vit_state_read(const void* d_state, fp8vit_state_view* out, voi
 
 /* Synchronous write of a whole state, the inverse of fp8vit_state_read: ring,
  * count, static values, last descales, last amax and flags are taken from
- * `in`; the internal atomic-max scratch and barrier words are cleared as by
+ * `in`; the internal atomic-max scratch and arrival counter are cleared as by
  * fp8vit_state_init. With it a calibration or a dynamic ring can be saved and
  * resumed: the forwards that follow behave as they would have in the process
  * that read the state. Ring, static, descale and amax entries must be finite

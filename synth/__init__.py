@@ -115,7 +115,8 @@ def _range(a: int, n: int = 16) -> Tuple[int, ...]:
 
 # The five workloads. Sizes: ViT attention with 16 heads; L=2304..16384 mirrors
 # the MI300X AITER table; hd128 at L=8192 mirrors the cuDNN kernel table; the
-# packed batch mixes three 14400-token images with eight 1024-token frames.
+# packed batch mixes three 14400-token images with eight 1024-token frames and
+# runs once with static scales and once with the dynamic ring.
 WORKLOADS = {
     "small_l256_hd72_dyn": Workload(
         "small_l256_hd72_dyn", (256,), 16, 72, "dynamic", 1, (),
@@ -136,4 +137,8 @@ WORKLOADS = {
         "packed_3x14400_8x1024_hd72", (14400, 14400, 14400) + (1024,) * 8, 16, 72, "static", 6,
         _range(6001), outlier_frac=0.001,
         description="packed batch 3x14400 + 8x1024 tokens, 16 heads, hd72, 0.1% outliers x20"),
+    "packed_3x14400_8x1024_hd72_dyn": Workload(
+        "packed_3x14400_8x1024_hd72_dyn", (14400, 14400, 14400) + (1024,) * 8, 16, 72, "dynamic", 6,
+        _range(6001), outlier_frac=0.001,
+        description="the same packed batch and input, dynamic scaling after 16 warm-ups"),
 }
