@@ -94,7 +94,7 @@ fp8vit_status attn_common(const void* q8, const void* k8, const void* v8, const 
       !aligned(d_cu_seqlens, 4) || !aligned(d_state, 256) || (out_fp8 && !aligned(d_out_descale, 4)))
     return FP8VIT_ERR_UNSUPPORTED;
   if (num_segments == 0 || total_tokens == 0 || max_seqlen == 0) return FP8VIT_OK;  // no rows to write
-  const int bm = fp8vit::attn_block_m(head_dim);
+  const int bm = fp8vit::attn_block_m(head_dim);   // the smallest shape: the most tiles
   const int64_t by_total = ((int64_t)total_tokens + bm - 1) / bm + num_segments;
   const int64_t by_max = (int64_t)num_segments * (((int64_t)max_seqlen + bm - 1) / bm);
   const int64_t ntiles = by_total < by_max ? by_total : by_max;
@@ -117,7 +117,7 @@ fp8vit_status attn_common(const void* q8, const void* k8, const void* v8, const 
   a.out_descale = d_out_descale;
   a.ld_out = ld_out;
   a.softmax_scale = softmax_scale > 0.0f ? softmax_scale : (float)(1.0 / std::sqrt((double)head_dim));
-  return from_hip(fp8vit::launch_attn(a, head_dim, total_tokens, as_stream(stream)));
+  return from_hip(fp8vit::launch_attn(a, head_dim, total_tokens, max_seqlen, as_stream(stream)));
 }
 }  // namespace
 

@@ -58,13 +58,25 @@ template <int D> struct Cfg;
 // chunks, so a row holds the head's D bytes followed by the first bytes of
 // the next head; those only ever meet zero Q bytes or discarded O columns).
 // NCB: 16-column blocks of O^T including the ones column.
-// WAVES x QB x 16 = BM queries per workgroup.
 template <> struct Cfg<72> {
   static constexpr int KS = 80, VS = 80, NCB = 5, ONES_CB = 4, ONES_LANE0 = 32;
-  static constexpr int WAVES = 8, QB = 1, MIN_WAVES_PER_EU = 4, BM = 128;
 };
 template <> struct Cfg<128> {
   static constexpr int KS = 144, VS = 144, NCB = 9, ONES_CB = 8, ONES_LANE0 = 0;
+};
+// Workgroup shapes: WAVES x QB x 16 = BM queries per workgroup, each wave
+// owning QB blocks of 16 queries that share every K and V operand it reads.
+// The wide hd72 shape (two query blocks per wave, 256 queries per workgroup,
+// 2 waves per SIMD) halves the LDS reads and the K/V staging per query; it is
+// used when the problem still gives every CU two workgroups.
+template <int D, bool WIDE> struct Shape;
+template <> struct Shape<72, false> {
+  static constexpr int WAVES = 8, QB = 1, MIN_WAVES_PER_EU = 4, BM = 128;
+};
+template <> struct Shape<72, true> {
+  static constexpr int WAVES = 8, QB = 2, MIN_WAVES_PER_EU = 2, BM = 256;
+};
+template <> struct Shape<128, false> {
   static constexpr int WAVES = 8, QB = 1, MIN_WAVES_PER_EU = 2, BM = 128;
 };
 
@@ -74,13 +86,13 @@ template <> struct Cfg<128> {
 //  V: key k sits in row k.
 __device__ __forceinline__ int k_key(int row) { return 32 * (row & 3) + (row >> 2); }
 
-template <int D> struct Stage {
-  static constexpr int THREADS = 64 * Cfg<D>::WAVES;
+template <int D, int WAVES> struct Stage {
+  static constexpr int THREADS = 64 * WAVES;
   static constexpr int KZERO = kBN * Cfg<D>::KS;                 // 32 zero bytes after the K rows
   static constexpr int KBUF = KZERO + 32, VBUF = kBN * Cfg<D>::VS;
   // DMA: one wave instruction moves 64 chunks of 16 bytes (1 KB) of a tile.
   static constexpr int NI = kBN * Cfg<D>::KS / 1024;              // instructions per K (or V) tile
-  static constexpr int NIW = (2 * NI + Cfg<D>::WAVES - 1) / Cfg<D>::WAVES;   // per wave, K and V together
+  static constexpr int NIW = (2 * NI + WAVES - 1) / WAVES;   // per wave, K and V together
   static_assert(kBN * Cfg<D>::KS % 1024 == 0 && Cfg<D>::KS == Cfg<D>::VS, "DMA tiling");
 };
 
@@ -154,14 +166,14 @@ __device__ __forceinline__ int2 probs_to_fp8(const v4f& s, float c, float nb, in
 // into kdst and, with_v, one V tile into vdst. Instruction i = wave + WAVES*n
 // of a tile moves chunks 64*i .. 64*i+63 of K (i < NI) or of V (NI <= i < 2 NI);
 // dma_off[n] holds the lane's global offset for tile 0.
-template <int D>
+template <int D, int WAVES>
 __device__ __forceinline__ void dma_issue(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
                                           const uint32_t* dma_off, int wave, uint32_t koff, uint8_t* kdst,
                                           uint32_t voff, uint8_t* vdst, bool with_v) {
-  using S = Stage<D>;
+  using S = Stage<D, WAVES>;
 #pragma unroll
   for (int n = 0; n < S::NIW; ++n) {
-    const int i = wave + Cfg<D>::WAVES * n;   // wave-uniform
+    const int i = wave + WAVES * n;   // wave-uniform
     if (i < S::NI) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kdst + 1024 * i), 16, dma_off[n] + koff, 0, 0, 0);
     } else if (i < 2 * S::NI && with_v) {
@@ -171,15 +183,16 @@ __device__ __forceinline__ void dma_issue(__amdgpu_buffer_rsrc_t krs, __amdgpu_b
   }
 }
 
-template <int D, bool OUT8>
-__global__ __launch_bounds__(64 * Cfg<D>::WAVES) __attribute__((amdgpu_waves_per_eu(Cfg<D>::MIN_WAVES_PER_EU)))
-void attn_kernel(AttnArgs a) {
+template <int D, bool OUT8, bool WIDE>
+__global__ __launch_bounds__((64 * Shape<D, WIDE>::WAVES))
+__attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn_kernel(AttnArgs a) {
   using C = Cfg<D>;
-  using S = Stage<D>;
-  constexpr int QB = C::QB;
+  using SH = Shape<D, WIDE>;
+  using S = Stage<D, SH::WAVES>;
+  constexpr int QB = SH::QB;
   constexpr int BMW = 16 * QB;
-  constexpr int kBM = C::BM;
-  static_assert(C::WAVES * BMW == kBM, "block shape");
+  constexpr int kBM = SH::BM;
+  static_assert(SH::WAVES * BMW == kBM, "block shape");
   // Two K and two V buffers, as separate objects: the compiler can then tell
   // the DMA's target apart from the buffer being read and does not wait for
   // the DMA before each LDS read.
@@ -225,7 +238,7 @@ void attn_kernel(AttnArgs a) {
   uint32_t dma_off[S::NIW];
 #pragma unroll
   for (int n = 0; n < S::NIW; ++n) {
-    const int i = wave + C::WAVES * n;
+    const int i = wave + SH::WAVES * n;
     const int ii = i < S::NI ? i : i - S::NI;
     const int c = 64 * ii + lane;
     const int row = c / (C::KS / 16), piece = c % (C::KS / 16);
@@ -234,7 +247,7 @@ void attn_kernel(AttnArgs a) {
   }
   // Issue this wave's DMA of K tile tk into kdst and (with_v) V tile tv into vdst.
   auto dma_tiles = [&](int tk, uint8_t* kdst, int tv, uint8_t* vdst, bool with_v) {
-    dma_issue<D>(krs, vrs, dma_off, wave, (uint32_t)tk * kBN * row_stride, kdst, (uint32_t)tv * kBN * row_stride,
+    dma_issue<D, SH::WAVES>(krs, vrs, dma_off, wave, (uint32_t)tk * kBN * row_stride, kdst, (uint32_t)tv * kBN * row_stride,
                  vdst, with_v);
   };
 
@@ -483,26 +496,53 @@ void attn_kernel(AttnArgs a) {
   }
 }
 
-int attn_block_m(int head_dim) { return head_dim == 72 ? Cfg<72>::BM : Cfg<128>::BM; }
+int attn_block_m(int head_dim) { return head_dim == 72 ? Shape<72, false>::BM : Shape<128, false>::BM; }
 
-hipError_t launch_attn(const AttnArgs& a, int head_dim, int total_tokens, hipStream_t s) {
+namespace {
+int g_cus[64];
+int device_cus() {
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  int& n = g_cus[dev & 63];
+  if (n == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) n = v;
+  }
+  return n;
+}
+
+// Upper bound on query tiles of BM rows per head: every segment adds at most
+// one partial tile.
+int64_t tiles_ub(int bm, int64_t total_tokens, int64_t nseg, int64_t max_seqlen) {
+  const int64_t by_total = (total_tokens + bm - 1) / bm + nseg;
+  const int64_t by_max = nseg * ((max_seqlen + bm - 1) / bm);
+  return by_total < by_max ? by_total : by_max;
+}
+
+template <int D, bool WIDE>
+hipError_t launch_shape(AttnArgs a, int total_tokens, int max_seqlen, hipStream_t s) {
+  a.ntiles_ub = (int32_t)tiles_ub(Shape<D, WIDE>::BM, total_tokens, a.nseg, max_seqlen);
   const int64_t items = (int64_t)a.H * a.ntiles_ub;
   const int64_t grid = ((items + 7) / 8) * 8;
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  (void)total_tokens;
-  const bool out8 = a.out8 != nullptr;
-  if (head_dim == 72) {
-    if (out8)
-      hipLaunchKernelGGL((attn_kernel<72, true>), dim3((unsigned)grid), dim3(64 * Cfg<72>::WAVES), 0, s, a);
-    else
-      hipLaunchKernelGGL((attn_kernel<72, false>), dim3((unsigned)grid), dim3(64 * Cfg<72>::WAVES), 0, s, a);
-  } else {
-    if (out8)
-      hipLaunchKernelGGL((attn_kernel<128, true>), dim3((unsigned)grid), dim3(64 * Cfg<128>::WAVES), 0, s, a);
-    else
-      hipLaunchKernelGGL((attn_kernel<128, false>), dim3((unsigned)grid), dim3(64 * Cfg<128>::WAVES), 0, s, a);
-  }
+  const dim3 block(64 * Shape<D, WIDE>::WAVES);
+  if (a.out8 != nullptr)
+    hipLaunchKernelGGL((attn_kernel<D, true, WIDE>), dim3((unsigned)grid), block, 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<D, false, WIDE>), dim3((unsigned)grid), block, 0, s, a);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_attn(const AttnArgs& a, int head_dim, int total_tokens, int max_seqlen, hipStream_t s) {
+  if (head_dim == 128) return launch_shape<128, false>(a, total_tokens, max_seqlen, s);
+  // The wide shape once its workgroups fill every CU twice (by the same upper
+  // bound on tiles the grid uses).
+  const int cus = device_cus();
+  if (cus == 0) return hipErrorInvalidDevice;
+  const int64_t wide_items = (int64_t)a.H * tiles_ub(Shape<72, true>::BM, total_tokens, a.nseg, max_seqlen);
+  if (wide_items >= 2 * (int64_t)cus) return launch_shape<72, true>(a, total_tokens, max_seqlen, s);
+  return launch_shape<72, false>(a, total_tokens, max_seqlen, s);
 }
 
 }  // namespace fp8vit

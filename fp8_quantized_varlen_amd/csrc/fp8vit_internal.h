@@ -50,7 +50,7 @@ struct AttnArgs {
   const int32_t* cu;
   int32_t nseg;
   int32_t H;
-  int32_t ntiles_ub;     // upper bound on query tiles per head
+  int32_t ntiles_ub;     // upper bound on query tiles per head (set by launch_attn)
   uint32_t tensor_bytes; // T * H * d: bytes of each of q8, k8, v8
   const DevState* st;
   uint16_t* out;           // bf16 output (out8 == nullptr)
@@ -59,7 +59,8 @@ struct AttnArgs {
   int64_t ld_out;          // token stride of the output, elements
   float softmax_scale;
 };
-hipError_t launch_attn(const AttnArgs& a, int head_dim, int total_tokens, hipStream_t s);
+// Picks the workgroup shape and sets a.ntiles_ub for it.
+hipError_t launch_attn(const AttnArgs& a, int head_dim, int total_tokens, int max_seqlen, hipStream_t s);
 int attn_block_m(int head_dim);
 
 }  // namespace fp8vit

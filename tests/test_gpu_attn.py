@@ -224,6 +224,31 @@ def test_attention_fp8_output_small(seglens, d):
     _check_fp8_output(codes8, o16, ref.out, out_descale, vmax_of(vb))
 
 
+# 64 heads make the grid wide enough (>= 2 workgroups of 256 queries per CU)
+# for the hd72 kernel's wide shape; the ragged segments (one token, empty,
+# partial tiles of both shapes) then run through it.
+WIDE_SEGLENS = (1500, 1, 733, 0, 257)
+
+
+def test_attention_wide_shape_ragged():
+    dev = require_gpu()
+    cu = make_cu_seqlens(WIDE_SEGLENS)
+    qb, kb, vb = make_qkv(91, int(cu[-1]), 64, 72)
+    check_vs_oracle(qb, kb, vb, cu, dev)
+
+
+def test_attention_wide_shape_fp8_output():
+    dev = require_gpu()
+    cu = make_cu_seqlens(WIDE_SEGLENS)
+    qb, kb, vb = make_qkv(92, int(cu[-1]), 64, 72)
+    ref = oracle.pipeline.forward(qb, kb, vb, cu, "dynamic", ring=oracle.scales.AmaxRing())
+    out_descale = float(np.float32(np.abs(ref.out).max() / 300.0))
+    codes8, o16, codes = _run_fp8out(qb, kb, vb, cu, dev, out_descale)
+    for c, r in zip(codes, ref.codes):
+        assert np.array_equal(codes_np(c), r)
+    _check_fp8_output(codes8, o16, ref.out, out_descale, vmax_of(vb))
+
+
 def test_attention_fp8_output_saturates_and_scales():
     """A descale too small for the output: every large element saturates to
     +-448 codes (0x7E / 0xFE), never NaN; a descale of 2x halves the codes' values."""
