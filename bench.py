@@ -173,7 +173,7 @@ def cpu_baseline(w, qb, kb, vb, static_values, out_gpu, target_s, compare=True):
             "gpu_rows_checked": int(sum(n for _, _, n, _, _ in rows_out))}
 
 
-def attn_kernel_name(w, dev):
+def attn_kernel_name(w, dev, out8):
     """Name of the attention kernel instance the library launches for this
     workload, as the profiler prints it: the hd72 wide shape (256 queries per
     workgroup) is used once the grid holds two of its workgroups per CU."""
@@ -184,7 +184,7 @@ def attn_kernel_name(w, dev):
         T, nseg, L = w.total_tokens, len(w.seglens), max(w.seglens)
         tiles = min((T + 255) // 256 + nseg, nseg * ((L + 255) // 256))
         wide = w.heads * tiles >= 2 * torch.cuda.get_device_properties(dev).multi_processor_count
-    return "attn_kernel<%d, false, %s>" % (d, "true" if wide else "false")
+    return "attn_kernel<%d, %s, %s>" % (d, "true" if out8 else "false", "true" if wide else "false")
 
 
 def attn_traffic(workload, head_dim):
@@ -339,7 +339,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4),
                      "traffic": attn_traffic(w.name, d),
-                     "kernel": attn_kernel_name(w, dev)},
+                     "kernel": attn_kernel_name(w, dev, args.out == "fp8")},
         "descale_used": state["descale_used"],
         **({"graph": {"ms_per_step": round(graph_ms, 4),
                       "value": round(w.flops / (graph_ms * 1e-3) / 1e12, 2)}} if graph_ms else {}),
