@@ -70,14 +70,19 @@ template <> struct Cfg<128> {
 // 2 waves per SIMD) halves the LDS reads and the K/V staging per query; it is
 // used when the problem still gives every CU two workgroups.
 template <int D, bool WIDE> struct Shape;
+// XT: the P.V products of tile j-1 run interleaved with the softmax of tile
+// j (a second P register set) instead of as a burst at the end of tile j-1.
 template <> struct Shape<72, false> {
   static constexpr int WAVES = 8, QB = 1, MIN_WAVES_PER_EU = 4, BM = 128;
+  static constexpr bool XT = false;
 };
 template <> struct Shape<72, true> {
   static constexpr int WAVES = 8, QB = 2, MIN_WAVES_PER_EU = 2, BM = 256;
+  static constexpr bool XT = false;
 };
 template <> struct Shape<128, false> {
   static constexpr int WAVES = 8, QB = 1, MIN_WAVES_PER_EU = 2, BM = 128;
+  static constexpr bool XT = true;
 };
 
 // LDS placement of a tile's rows.
@@ -251,7 +256,7 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
                  vdst, with_v);
   };
 
-  dma_tiles(0, k_lds0, 0, v_lds0, true);    // K(0), V(0)
+  dma_tiles(0, k_lds0, 0, v_lds0, !SH::XT);    // K(0), and V(0) unless iteration 0 loads it
   dma_tiles(1, k_lds1, 0, v_lds0, false);   // K(1)
   // Zero the 32 bytes after each K tile (read only against zero Q bytes).
   for (int r = tid; r < 2 * 4; r += S::THREADS)
@@ -443,18 +448,158 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) o[qb][C::NCB - 1] = mfma_fp8(vprev, plo[qb], o[qb][C::NCB - 1]);
   };
+  // Cross-tile variant: iteration j reads K(j+1) and V(j-1) while the DMA
+  // fills the other buffer of each pair with K(j+2) and V(j); its steps run
+  // O^T += V(j-1)^T P(j-1)^T block by block next to the softmax of S(j), so P
+  // lives in two register sets. A rescale found at the start of iteration j
+  // is applied at its end, after the products of P(j-1) (formed with the old
+  // reference max) have been added.
+  struct PSet { v8i hi[QB], lo[QB]; };
+  PSet pa, pb;
+  auto pv_block = [&](const PSet& pp, const v8i& vop, int cb) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) o[qb][cb] = mfma_fp8(vop, pp.hi[qb], o[qb][cb]);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) o[qb][cb] = mfma_fp8(vop, pp.lo[qb], o[qb][cb]);
+  };
+  auto iteration_xt = [&](auto first_c, auto last_c, auto odd_c, int j, PSet& cur, const PSet& prev) {
+    constexpr bool FIRST = decltype(first_c)::value;
+    constexpr bool LAST = decltype(last_c)::value;
+    constexpr bool ODD = decltype(odd_c)::value;
+    uint8_t* const k_fill = ODD ? k_lds1 : k_lds0;         // K(j+2)
+    uint8_t* const v_fill = ODD ? v_lds1 : v_lds0;         // V(j)
+    const uint8_t* const k_read = ODD ? k_lds0 : k_lds1;   // K(j+1)
+    const uint8_t* const v_read = ODD ? v_lds0 : v_lds1;   // V(j-1)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    dma_tiles(j + 2, k_fill, j, v_fill, true);
+    if (LAST) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            sc[qb][t][r] = (j * kBN + 32 * g + 4 * t + r >= L) ? -INFINITY : sc[qb][t][r];
+    }
+    float lm[QB];
+    bool over = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 8; t += 2) {
+        m0 = fmaxf(fmaxf(fmaxf(fmaxf(m0, sc[qb][t][0]), sc[qb][t][1]), sc[qb][t][2]), sc[qb][t][3]);
+        m1 = fmaxf(fmaxf(fmaxf(fmaxf(m1, sc[qb][t + 1][0]), sc[qb][t + 1][1]), sc[qb][t + 1][2]), sc[qb][t + 1][3]);
+      }
+      lm[qb] = fmaxf(m0, m1);
+      over = over || (lm[qb] > thr[qb]);
+    }
+    const bool rescale = __ballot(over) != 0ull;
+    float alpha[QB];
+    if (rescale) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float m = lm[qb];
+        m = fmaxf(m, __shfl_xor(m, 16, 64));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        const float mn = fmaxf(mref[qb], m * cexp);
+        alpha[qb] = __builtin_amdgcn_exp2f(mref[qb] - mn);
+        mref[qb] = mn;
+        thr[qb] = (mn + kLazy) / cexp;
+      }
+    }
+    float nb[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) nb[qb] = kExpBias - mref[qb];
+
+    uint32_t kbase = (uint32_t)kl_lane, vbase = (uint32_t)vl_lane;
+    asm volatile("" : "+v"(kbase), "+v"(vbase));
+    const lds_u8* kl = (const lds_u8*)k_read + kbase;
+    const lds_u8* vl = (const lds_u8*)v_read + vbase;
+    v8i kop, vop;
+    if (!LAST) kop = k_operand<D>(kl, 0);
+    if (!FIRST) vop = v_op(vl, 0);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (!FIRST) {
+        if (t < C::NCB) {
+          const v8i vcur = vop;
+          if (t + 1 < C::NCB) vop = v_op(vl, t + 1);
+          pv_block(prev, vcur, t);
+        }
+        if (t == 7 && C::NCB > 8) pv_block(prev, vop, 8);
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int2 p = probs_to_fp8(sc[qb][t], cexp, nb[qb], cur.hi[qb][t], cur.lo[qb][t]);
+        cur.hi[qb][t] = p.x;
+        cur.lo[qb][t] = p.y;
+        // consumed only by the next iteration: keep its computation here
+        asm volatile("" : "+v"(cur.hi[qb]), "+v"(cur.lo[qb]));
+      }
+      if (!LAST) {
+        const v8i kcur = kop;
+        if (t + 1 < 8) kop = k_operand<D>(kl, t + 1);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sc[qb][t] = mfma_fp8(kcur, qop[qb], zero4);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (rescale) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int cb = 0; cb < C::NCB; ++cb) o[qb][cb] *= alpha[qb];
+    }
+  };
+  // P.V of the last tile J; its V was loaded by iteration J into buffer J % 2.
+  auto final_pv = [&](const PSet& pp, const uint8_t* vbuf) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    uint32_t vbase = (uint32_t)vl_lane;
+    asm volatile("" : "+v"(vbase));
+    const lds_u8* vl = (const lds_u8*)vbuf + vbase;
+#pragma unroll
+    for (int cb = 0; cb < C::NCB; ++cb) pv_block(pp, v_op(vl, cb), cb);
+  };
+
   using T_ = std::true_type;
   using F_ = std::false_type;
-  int j = 0;
-  for (; j + 2 < ntiles; j += 2) {
-    iteration(F_{}, F_{}, j);
-    iteration(F_{}, T_{}, j + 1);
-  }
-  if (j + 1 < ntiles) {
-    iteration(F_{}, F_{}, j);
-    iteration(T_{}, T_{}, j + 1);
+  if constexpr (!SH::XT) {
+    int j = 0;
+    for (; j + 2 < ntiles; j += 2) {
+      iteration(F_{}, F_{}, j);
+      iteration(F_{}, T_{}, j + 1);
+    }
+    if (j + 1 < ntiles) {
+      iteration(F_{}, F_{}, j);
+      iteration(T_{}, T_{}, j + 1);
+    } else {
+      iteration(T_{}, F_{}, j);
+    }
   } else {
-    iteration(T_{}, F_{}, j);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) pa.hi[qb] = pa.lo[qb] = pb.hi[qb] = pb.lo[qb] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    if (ntiles == 1) {
+      iteration_xt(T_{}, T_{}, F_{}, 0, pa, pb);
+      final_pv(pa, v_lds0);
+    } else {
+      iteration_xt(T_{}, F_{}, F_{}, 0, pa, pb);
+      int j = 1;
+      for (; j + 2 < ntiles; j += 2) {
+        iteration_xt(F_{}, F_{}, T_{}, j, pb, pa);
+        iteration_xt(F_{}, F_{}, F_{}, j + 1, pa, pb);
+      }
+      if (j + 1 < ntiles) {
+        iteration_xt(F_{}, F_{}, T_{}, j, pb, pa);
+        iteration_xt(F_{}, T_{}, F_{}, j + 1, pa, pb);
+        final_pv(pa, v_lds0);
+      } else {
+        iteration_xt(F_{}, T_{}, T_{}, j, pb, pa);
+        final_pv(pb, v_lds1);
+      }
+    }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no DMA in flight past the loop
 
