@@ -427,9 +427,11 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) sc[qb][t] = mfma_fp8(kcur, qop[qb], zero4);
       }
-      // keep the steps apart: hoisting later LDS reads or softmax work into
-      // this step would raise register pressure
-      __builtin_amdgcn_sched_barrier(0);
+      // One query block per wave (4 waves/SIMD, 128 VGPRs): keep the steps
+      // apart, since hoisting later LDS reads or softmax work into this step
+      // would spill. Two query blocks (256 VGPRs): let the scheduler overlap
+      // adjacent steps (+1 %).
+      if (QB == 1) __builtin_amdgcn_sched_barrier(0);
     }
     // O^T += V(j)^T P(j)^T, block cb's lo term issued after block cb+1's hi
     // term, so no product waits on the one just issued.
