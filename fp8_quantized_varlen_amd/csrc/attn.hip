@@ -58,11 +58,12 @@ template <int D> struct Cfg;
 // chunks, so a row holds the head's D bytes followed by the first bytes of
 // the next head; those only ever meet zero Q bytes or discarded O columns).
 // NCB: 16-column blocks of O^T including the ones column.
+// VH_COLS: V columns held in the widened (f16, transposed) tile.
 template <> struct Cfg<72> {
-  static constexpr int KS = 80, VS = 80, NCB = 5, ONES_CB = 4, ONES_LANE0 = 32;
+  static constexpr int KS = 80, VS = 80, NCB = 5, ONES_CB = 4, ONES_LANE0 = 32, VH_COLS = 80;
 };
 template <> struct Cfg<128> {
-  static constexpr int KS = 144, VS = 144, NCB = 9, ONES_CB = 8, ONES_LANE0 = 0;
+  static constexpr int KS = 144, VS = 144, NCB = 9, ONES_CB = 8, ONES_LANE0 = 0, VH_COLS = 128;
 };
 // Workgroup shapes: WAVES x QB x 16 = BM queries per workgroup, each wave
 // owning QB blocks of 16 queries that share every K and V operand it reads.
@@ -72,17 +73,20 @@ template <> struct Cfg<128> {
 template <int D, bool WIDE> struct Shape;
 // XT: the P.V products of tile j-1 run interleaved with the softmax of tile
 // j (a second P register set) instead of as a burst at the end of tile j-1.
+// P16: P~ goes to the P.V product as one f16 term on the f16 MFMA, with V
+// widened once per tile into a transposed f16 copy in LDS (instead of two
+// e4m3 terms against e4m3 V).
 template <> struct Shape<72, false> {
   static constexpr int WAVES = 8, QB = 1, MIN_WAVES_PER_EU = 4, BM = 128;
-  static constexpr bool XT = false;
+  static constexpr bool XT = false, P16 = false;
 };
 template <> struct Shape<72, true> {
   static constexpr int WAVES = 8, QB = 2, MIN_WAVES_PER_EU = 2, BM = 256;
-  static constexpr bool XT = false;
+  static constexpr bool XT = false, P16 = true;
 };
 template <> struct Shape<128, false> {
   static constexpr int WAVES = 8, QB = 1, MIN_WAVES_PER_EU = 2, BM = 128;
-  static constexpr bool XT = true;
+  static constexpr bool XT = true, P16 = false;
 };
 
 // LDS placement of a tile's rows.
@@ -95,6 +99,10 @@ template <int D, int WAVES> struct Stage {
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int KZERO = kBN * Cfg<D>::KS;                 // 32 zero bytes after the K rows
   static constexpr int KBUF = KZERO + 32, VBUF = kBN * Cfg<D>::VS;
+  // Widened V: column c holds the tile's 128 keys as f16 at byte 2*key of row
+  // c; rows are VHS bytes apart (16 B of padding: the 16 lanes of a lane
+  // group, one column each, read 16 B at distinct bank offsets).
+  static constexpr int VHS = 2 * kBN + 16, VHBUF = Cfg<D>::VH_COLS * VHS;
   // DMA: one wave instruction moves 64 chunks of 16 bytes (1 KB) of a tile.
   static constexpr int NI = kBN * Cfg<D>::KS / 1024;              // instructions per K (or V) tile
   static constexpr int NIW = (2 * NI + WAVES - 1) / WAVES;   // per wave, K and V together
@@ -146,6 +154,49 @@ __device__ __forceinline__ v8i v_operand(const lds_u8* vl, int cb) {
     r[2 * sidx + 1] = x[1];
   }
   return r;
+}
+
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v8h lds_v8h;
+
+// One wave's share of widening an e4m3 V tile (row-major, VS-byte rows) into
+// the transposed f16 tile. Unit i = (column block cb, 8-key step sidx) is one
+// byte-transposing read: lane (g, i16) gets keys 32g + 8 sidx .. + 7 of
+// column 16 cb + i16, converts them and stores 16 B. hd72: column 72 becomes
+// 1.0 (the row-sum column) and columns 73..79 zero.
+template <int D, int WAVES>
+__device__ __forceinline__ void widen_v(const uint8_t* v8, uint8_t* vh, int wave, int g, int i16, int vl_lane) {
+  constexpr int NU = (Cfg<D>::VH_COLS / 16) * 4;
+#pragma unroll
+  for (int n = 0; n < (NU + WAVES - 1) / WAVES; ++n) {
+    const int i = wave + WAVES * n;   // wave-uniform
+    if (i < NU) {
+      const int cb = i >> 2, sidx = i & 3;
+      const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (lds_v2i*)((const lds_u8*)v8 + vl_lane + 8 * sidx * Cfg<D>::VS + 16 * cb));
+      const int col = 16 * cb + i16;
+      v4i y;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        y[2 * h] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[h], 1.0f, false));
+        y[2 * h + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[h], 1.0f, true));
+      }
+      if (D == 72 && col >= 72) {
+        const int f = col == 72 ? 0x3c003c00 : 0;
+        y = v4i{f, f, f, f};
+      }
+      *(lds_v4i*)((lds_u8*)vh + col * Stage<D, WAVES>::VHS + 2 * (32 * g + 8 * sidx)) = y;
+    }
+  }
+}
+
+// A operand of the f16 product of column block cb and 32-key chunk c: lane
+// (g, i16) reads keys 32g + 8c .. + 7 of column 16 cb + i16. `vhl` is the
+// lane's byte offset for cb = c = 0.
+template <int D, int WAVES>
+__device__ __forceinline__ v8h vh_operand(const lds_u8* vhl, int cb, int c) {
+  return *(const lds_v8h*)(vhl + 16 * cb * Stage<D, WAVES>::VHS + 16 * c);
 }
 
 // Two e4m3 terms of four probabilities P~ = exp2(s*c + nb), packed as one
@@ -205,6 +256,8 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[S::KBUF];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[S::VBUF];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[S::VBUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t vh_lds0[SH::P16 ? S::VHBUF : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t vh_lds1[SH::P16 ? S::VHBUF : 16];
 
   // ---- work item: XCD-grouped (head, query tile) -> segment by prefix scan ----
   const int G = gridDim.x;
@@ -257,7 +310,7 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
   };
 
   dma_tiles(0, k_lds0, 0, v_lds0, !SH::XT);    // K(0), and V(0) unless iteration 0 loads it
-  dma_tiles(1, k_lds1, 0, v_lds0, false);   // K(1)
+  dma_tiles(1, k_lds1, 1, v_lds1, SH::P16);    // K(1), and V(1) for the widening pipeline
   // Zero the 32 bytes after each K tile (read only against zero Q bytes).
   for (int r = tid; r < 2 * 4; r += S::THREADS)
     *reinterpret_cast<uint2*>((r < 4 ? k_lds0 : k_lds1) + S::KZERO + 8 * (r % 4)) = make_uint2(0u, 0u);
@@ -308,6 +361,8 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
   __syncthreads();
   const int kl_lane = k_lane_offset<D>(g, i16);
   const int vl_lane = v_lane_offset<D>(g, i16);
+  const int vhl_lane = i16 * S::VHS + 64 * g;
+  if constexpr (SH::P16) widen_v<D, SH::WAVES>(v_lds0, vh_lds0, wave, g, i16, vl_lane);   // V(0)
 
   // Software pipeline over key tiles. Iteration j holds S(j) in registers
   // (computed during iteration j-1), so the tile's maximum is known before
@@ -450,6 +505,107 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) o[qb][C::NCB - 1] = mfma_fp8(vprev, plo[qb], o[qb][C::NCB - 1]);
   };
+  // f16 P variant: iteration j reads K(j+1), the widened V(j) and the e4m3
+  // V(j+1) (which it widens into the other f16 buffer), while the DMA fills
+  // the other K buffer with K(j+2) and the other e4m3 V buffer with V(j+2).
+  // P(j) becomes f16: for 32-key chunk c the lane packs its rows of S^T
+  // blocks 2c and 2c+1, keys 32g + 8c .. + 7, which is the B operand of the
+  // 16x16x32 f16 product whose A operand is the widened V^T.
+  int p16[QB][16];
+  auto iteration_p16 = [&](auto last_c, auto odd_c, int j) {
+    constexpr bool LAST = decltype(last_c)::value;
+    constexpr bool ODD = decltype(odd_c)::value;
+    uint8_t* const k_fill = ODD ? k_lds1 : k_lds0;          // K(j+2)
+    uint8_t* const v_fill = ODD ? v_lds1 : v_lds0;          // e4m3 V(j+2)
+    const uint8_t* const v_conv = ODD ? v_lds0 : v_lds1;    // e4m3 V(j+1)
+    uint8_t* const vh_fill = ODD ? vh_lds0 : vh_lds1;       // f16 V(j+1)
+    const uint8_t* const k_read = ODD ? k_lds0 : k_lds1;    // K(j+1)
+    const uint8_t* const vh_read = ODD ? vh_lds1 : vh_lds0; // f16 V(j)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    dma_tiles(j + 2, k_fill, j + 2, v_fill, true);
+    if (!LAST) widen_v<D, SH::WAVES>(v_conv, vh_fill, wave, g, i16, vl_lane);
+    if (LAST) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            sc[qb][t][r] = (j * kBN + 32 * g + 4 * t + r >= L) ? -INFINITY : sc[qb][t][r];
+    }
+    float lm[QB];
+    bool over = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 8; t += 2) {
+        m0 = fmaxf(fmaxf(fmaxf(fmaxf(m0, sc[qb][t][0]), sc[qb][t][1]), sc[qb][t][2]), sc[qb][t][3]);
+        m1 = fmaxf(fmaxf(fmaxf(fmaxf(m1, sc[qb][t + 1][0]), sc[qb][t + 1][1]), sc[qb][t + 1][2]), sc[qb][t + 1][3]);
+      }
+      lm[qb] = fmaxf(m0, m1);
+      over = over || (lm[qb] > thr[qb]);
+    }
+    if (__ballot(over) != 0ull) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float m = lm[qb];
+        m = fmaxf(m, __shfl_xor(m, 16, 64));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        const float mn = fmaxf(mref[qb], m * cexp);
+        const float alpha = __builtin_amdgcn_exp2f(mref[qb] - mn);
+        mref[qb] = mn;
+        thr[qb] = (mn + kLazy) / cexp;
+#pragma unroll
+        for (int cb = 0; cb < C::NCB; ++cb) o[qb][cb] *= alpha;
+      }
+    }
+    float nb[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) nb[qb] = kExpBias - mref[qb];
+
+    uint32_t kbase = (uint32_t)kl_lane, vbase = (uint32_t)vhl_lane;
+    asm volatile("" : "+v"(kbase), "+v"(vbase));
+    const lds_u8* kl = (const lds_u8*)k_read + kbase;
+    const lds_u8* vhl = (const lds_u8*)vh_read + vbase;
+    v8i kop;
+    if (!LAST) kop = k_operand<D>(kl, 0);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[qb][t][0], cexp, nb[qb]));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[qb][t][1], cexp, nb[qb]));
+        const float p2 = __builtin_amdgcn_exp2f(fmaf(sc[qb][t][2], cexp, nb[qb]));
+        const float p3 = __builtin_amdgcn_exp2f(fmaf(sc[qb][t][3], cexp, nb[qb]));
+        p16[qb][2 * t] = __builtin_bit_cast(int, (v2h){(_Float16)p0, (_Float16)p1});
+        p16[qb][2 * t + 1] = __builtin_bit_cast(int, (v2h){(_Float16)p2, (_Float16)p3});
+      }
+      if (!LAST) {
+        const v8i kcur = kop;
+        if (t + 1 < 8) kop = k_operand<D>(kl, t + 1);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sc[qb][t] = mfma_fp8(kcur, qop[qb], zero4);
+      }
+      if (QB == 1) __builtin_amdgcn_sched_barrier(0);
+    }
+    // O^T += V(j)^T P(j)^T: per column block, four 32-key chunks.
+#pragma unroll
+    for (int cb = 0; cb < C::NCB; ++cb) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const v8h va = vh_operand<D, SH::WAVES>(vhl, cb, c);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const v8h pb = __builtin_bit_cast(
+              v8h, v4i{p16[qb][4 * c], p16[qb][4 * c + 1], p16[qb][4 * c + 2], p16[qb][4 * c + 3]});
+          o[qb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, o[qb][cb], 0, 0, 0);
+        }
+      }
+    }
+  };
+
   // Cross-tile variant: iteration j reads K(j+1) and V(j-1) while the DMA
   // fills the other buffer of each pair with K(j+2) and V(j); its steps run
   // O^T += V(j-1)^T P(j-1)^T block by block next to the softmax of S(j), so P
@@ -568,7 +724,19 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
 
   using T_ = std::true_type;
   using F_ = std::false_type;
-  if constexpr (!SH::XT) {
+  if constexpr (SH::P16) {
+    int j = 0;
+    for (; j + 2 < ntiles; j += 2) {
+      iteration_p16(F_{}, F_{}, j);
+      iteration_p16(F_{}, T_{}, j + 1);
+    }
+    if (j + 1 < ntiles) {
+      iteration_p16(F_{}, F_{}, j);
+      iteration_p16(T_{}, T_{}, j + 1);
+    } else {
+      iteration_p16(T_{}, F_{}, j);
+    }
+  } else if constexpr (!SH::XT) {
     int j = 0;
     for (; j + 2 < ntiles; j += 2) {
       iteration(F_{}, F_{}, j);
