@@ -588,21 +588,22 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) sc[qb][t] = mfma_fp8(kcur, qop[qb], zero4);
       }
-      if (QB == 1) __builtin_amdgcn_sched_barrier(0);
-    }
-    // O^T += V(j)^T P(j)^T: per column block, four 32-key chunks.
+      // O^T += V(j)^T P(j)^T for the 32-key chunk whose P is now complete,
+      // so the P.V products spread over the softmax work of the tile.
+      if (t & 1) {
+        const int c = t >> 1;
 #pragma unroll
-    for (int cb = 0; cb < C::NCB; ++cb) {
+        for (int cb = 0; cb < C::NCB; ++cb) {
+          const v8h va = vh_operand<D, SH::WAVES>(vhl, cb, c);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const v8h va = vh_operand<D, SH::WAVES>(vhl, cb, c);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const v8h pb = __builtin_bit_cast(
-              v8h, v4i{p16[qb][4 * c], p16[qb][4 * c + 1], p16[qb][4 * c + 2], p16[qb][4 * c + 3]});
-          o[qb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, o[qb][cb], 0, 0, 0);
+          for (int qb = 0; qb < QB; ++qb) {
+            const v8h pb = __builtin_bit_cast(
+                v8h, v4i{p16[qb][4 * c], p16[qb][4 * c + 1], p16[qb][4 * c + 2], p16[qb][4 * c + 3]});
+            o[qb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, o[qb][cb], 0, 0, 0);
+          }
         }
       }
+      if (QB == 1) __builtin_amdgcn_sched_barrier(0);
     }
   };
 
