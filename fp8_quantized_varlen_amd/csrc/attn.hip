@@ -69,7 +69,7 @@ template <> struct Cfg<128> {
 // owning QB blocks of 16 queries that share every K and V operand it reads.
 // The wide hd72 shape (two query blocks per wave, 256 queries per workgroup,
 // 2 waves per SIMD) halves the LDS reads and the K/V staging per query; it is
-// used when the problem still gives every CU two workgroups.
+// used unless the problem is too small to spread its workgroups over the chip.
 template <int D, bool WIDE> struct Shape;
 // XT: the P.V products of tile j-1 run interleaved with the softmax of tile
 // j (a second P register set) instead of as a burst at the end of tile j-1.
@@ -852,12 +852,13 @@ hipError_t launch_shape(AttnArgs a, int total_tokens, int max_seqlen, hipStream_
 
 hipError_t launch_attn(const AttnArgs& a, int head_dim, int total_tokens, int max_seqlen, hipStream_t s) {
   if (head_dim == 128) return launch_shape<128, false>(a, total_tokens, max_seqlen, s);
-  // The wide shape once its workgroups fill every CU twice (by the same upper
-  // bound on tiles the grid uses).
+  // The wide shape once its workgroups occupy at least half of the CUs (by
+  // the same upper bound on tiles the grid uses): measured faster from 144
+  // workgroups on 256 CUs (L = 2304, 16 heads) up, slower at 16 (L = 256).
   const int cus = device_cus();
   if (cus == 0) return hipErrorInvalidDevice;
   const int64_t wide_items = (int64_t)a.H * tiles_ub(Shape<72, true>::BM, total_tokens, a.nseg, max_seqlen);
-  if (wide_items >= 2 * (int64_t)cus) return launch_shape<72, true>(a, total_tokens, max_seqlen, s);
+  if (2 * wide_items >= (int64_t)cus) return launch_shape<72, true>(a, total_tokens, max_seqlen, s);
   return launch_shape<72, false>(a, total_tokens, max_seqlen, s);
 }
 

@@ -224,9 +224,10 @@ def test_attention_fp8_output_small(seglens, d):
     _check_fp8_output(codes8, o16, ref.out, out_descale, vmax_of(vb))
 
 
-# 64 heads make the grid wide enough (>= 2 workgroups of 256 queries per CU)
-# for the hd72 kernel's wide shape; the ragged segments (one token, empty,
-# partial tiles of both shapes) then run through it.
+# 64 heads make the grid wide enough (workgroups of 256 queries on at least
+# half of the CUs) for the hd72 kernel's wide shape; the ragged segments (one
+# token, empty, partial tiles of both shapes) then run through it. The small
+# cases above run the narrow shape.
 WIDE_SEGLENS = (1500, 1, 733, 0, 257)
 
 
