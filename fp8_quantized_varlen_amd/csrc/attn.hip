@@ -28,8 +28,11 @@
 //    the VALU forms P(j). Lazy reference max m_ref: P~ = 2^7 * exp2(t - m_ref)
 //    and m_ref moves only when a score exceeds m_ref + 1.75 (P~ could then pass
 //    448, e4m3's largest value); O is rescaled at the end of that iteration.
-//  * P~ goes to the FP8 MFMA as two e4m3 terms, hi = e4m3(P~) and
-//    lo = e4m3(P~ - hi): a single e4m3 term adds ~2.5% relative error to O.
+//  * P~ needs more than e4m3 precision (a single e4m3 term adds ~2.5%
+//    relative error to O). The wide hd72 shape rounds it once to f16 and runs
+//    P.V on the f16 MFMA against V widened (exactly) into a transposed f16
+//    copy in LDS; the other shapes give the FP8 MFMA two e4m3 terms,
+//    hi = e4m3(P~) and lo = e4m3(P~ - hi).
 //  * Work items are (head, query tile); consecutive items of one head are
 //    mapped to the same XCD so that K/V re-reads hit that XCD's L2.
 #include <type_traits>
