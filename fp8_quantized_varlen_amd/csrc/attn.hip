@@ -102,10 +102,11 @@ template <int D, int WAVES> struct Stage {
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int KZERO = kBN * Cfg<D>::KS;                 // 32 zero bytes after the K rows
   static constexpr int KBUF = KZERO + 32, VBUF = kBN * Cfg<D>::VS;
-  // Widened V: column c holds the tile's 128 keys as f16 at byte 2*key of row
-  // c; rows are VHS bytes apart (16 B of padding: the 16 lanes of a lane
-  // group, one column each, read 16 B at distinct bank offsets).
-  static constexpr int VHS = 2 * kBN + 16, VHBUF = Cfg<D>::VH_COLS * VHS;
+  // Widened V, f16, in the order of the operand reads: the 16-byte chunk of
+  // column 16 cb + i16 holding keys 32 g + 8 c .. + 7 sits at
+  // ((4 cb + c) * 64 + 16 g + i16) * 16, so that every read (and every
+  // widening store) of a wave is one contiguous kilobyte.
+  static constexpr int VHBUF = (Cfg<D>::VH_COLS / 16) * 4 * 1024;
   // DMA: one wave instruction moves 64 chunks of 16 bytes (1 KB) of a tile.
   static constexpr int NI = kBN * Cfg<D>::KS / 1024;              // instructions per K (or V) tile
   static constexpr int NIW = (2 * NI + WAVES - 1) / WAVES;   // per wave, K and V together
@@ -164,10 +165,10 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v8h lds_v8h;
 
 // One wave's share of widening an e4m3 V tile (row-major, VS-byte rows) into
-// the transposed f16 tile. Unit i = (column block cb, 8-key step sidx) is one
+// the f16 tile. Unit i = (column block cb, 8-key step sidx) is one
 // byte-transposing read: lane (g, i16) gets keys 32g + 8 sidx .. + 7 of
-// column 16 cb + i16, converts them and stores 16 B. hd72: column 72 becomes
-// 1.0 (the row-sum column) and columns 73..79 zero.
+// column 16 cb + i16, converts them and stores its 16 B at 1024 i + 16 lane.
+// hd72: column 72 becomes 1.0 (the row-sum column) and columns 73..79 zero.
 template <int D, int WAVES>
 __device__ __forceinline__ void widen_v(const uint8_t* v8, uint8_t* vh, int wave, int g, int i16, int vl_lane) {
   constexpr int NU = (Cfg<D>::VH_COLS / 16) * 4;
@@ -189,17 +190,16 @@ __device__ __forceinline__ void widen_v(const uint8_t* v8, uint8_t* vh, int wave
         const int f = col == 72 ? 0x3c003c00 : 0;
         y = v4i{f, f, f, f};
       }
-      *(lds_v4i*)((lds_u8*)vh + col * Stage<D, WAVES>::VHS + 2 * (32 * g + 8 * sidx)) = y;
+      *(lds_v4i*)((lds_u8*)vh + 1024 * i + 16 * (16 * g + i16)) = y;
     }
   }
 }
 
 // A operand of the f16 product of column block cb and 32-key chunk c: lane
 // (g, i16) reads keys 32g + 8c .. + 7 of column 16 cb + i16. `vhl` is the
-// lane's byte offset for cb = c = 0.
-template <int D, int WAVES>
+// lane's byte offset (16 * lane).
 __device__ __forceinline__ v8h vh_operand(const lds_u8* vhl, int cb, int c) {
-  return *(const lds_v8h*)(vhl + 16 * cb * Stage<D, WAVES>::VHS + 16 * c);
+  return *(const lds_v8h*)(vhl + 1024 * (4 * cb + c));
 }
 
 // Two e4m3 terms of four probabilities P~ = exp2(s*c + nb), packed as one
@@ -364,7 +364,7 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
   __syncthreads();
   const int kl_lane = k_lane_offset<D>(g, i16);
   const int vl_lane = v_lane_offset<D>(g, i16);
-  const int vhl_lane = i16 * S::VHS + 64 * g;
+  const int vhl_lane = 16 * lane;
   if constexpr (SH::P16) widen_v<D, SH::WAVES>(v_lds0, vh_lds0, wave, g, i16, vl_lane);   // V(0)
 
   // Software pipeline over key tiles. Iteration j holds S(j) in registers
@@ -597,7 +597,7 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
         const int c = t >> 1;
 #pragma unroll
         for (int cb = 0; cb < C::NCB; ++cb) {
-          const v8h va = vh_operand<D, SH::WAVES>(vhl, cb, c);
+          const v8h va = vh_operand(vhl, cb, c);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
             const v8h pb = __builtin_bit_cast(
