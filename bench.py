@@ -175,15 +175,13 @@ def cpu_baseline(w, qb, kb, vb, static_values, out_gpu, target_s, compare=True):
 
 def attn_kernel_name(w, dev, out8):
     """Name of the attention kernel instance the library launches for this
-    workload, as the profiler prints it: the hd72 wide shape (256 queries per
+    workload, as the profiler prints it: the wide shape (256 queries per
     workgroup) is used once its workgroups cover at least half of the CUs."""
     import torch
     d = w.head_dim
-    wide = False
-    if d == 72:
-        T, nseg, L = w.total_tokens, len(w.seglens), max(w.seglens)
-        tiles = min((T + 255) // 256 + nseg, nseg * ((L + 255) // 256))
-        wide = 2 * w.heads * tiles >= torch.cuda.get_device_properties(dev).multi_processor_count
+    T, nseg, L = w.total_tokens, len(w.seglens), max(w.seglens)
+    tiles = min((T + 255) // 256 + nseg, nseg * ((L + 255) // 256))
+    wide = 2 * w.heads * tiles >= torch.cuda.get_device_properties(dev).multi_processor_count
     return "attn_kernel<%d, %s, %s>" % (d, "true" if out8 else "false", "true" if wide else "false")
 
 

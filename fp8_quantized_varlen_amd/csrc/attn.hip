@@ -29,10 +29,10 @@
 //    and m_ref moves only when a score exceeds m_ref + 1.75 (P~ could then pass
 //    448, e4m3's largest value); O is rescaled at the end of that iteration.
 //  * P~ needs more than e4m3 precision (a single e4m3 term adds ~2.5%
-//    relative error to O). The wide hd72 shape rounds it once to f16 and runs
-//    P.V on the f16 MFMA against V widened (exactly) into a transposed f16
-//    copy in LDS; the other shapes give the FP8 MFMA two e4m3 terms,
-//    hi = e4m3(P~) and lo = e4m3(P~ - hi).
+//    relative error to O). The wide shapes round it once to f16 and run P.V
+//    on the f16 MFMA against V widened (exactly) into an f16 copy in LDS; the
+//    narrow shapes give the FP8 MFMA two e4m3 terms, hi = e4m3(P~) and
+//    lo = e4m3(P~ - hi).
 //  * Work items are (head, query tile); consecutive items of one head are
 //    mapped to the same XCD so that K/V re-reads hit that XCD's L2.
 #include <type_traits>
@@ -70,9 +70,10 @@ template <> struct Cfg<128> {
 };
 // Workgroup shapes: WAVES x QB x 16 = BM queries per workgroup, each wave
 // owning QB blocks of 16 queries that share every K and V operand it reads.
-// The wide hd72 shape (two query blocks per wave, 256 queries per workgroup,
-// 2 waves per SIMD) halves the LDS reads and the K/V staging per query; it is
-// used unless the problem is too small to spread its workgroups over the chip.
+// The wide shapes (two query blocks per wave, 256 queries per workgroup,
+// 2 waves per SIMD) halve the LDS reads and the K/V staging per query; they
+// are used unless the problem is too small to spread their workgroups over
+// the chip.
 template <int D, bool WIDE> struct Shape;
 // XT: the P.V products of tile j-1 run interleaved with the softmax of tile
 // j (a second P register set) instead of as a burst at the end of tile j-1.
@@ -90,6 +91,10 @@ template <> struct Shape<72, true> {
 template <> struct Shape<128, false> {
   static constexpr int WAVES = 8, QB = 1, MIN_WAVES_PER_EU = 2, BM = 128;
   static constexpr bool XT = true, P16 = false;
+};
+template <> struct Shape<128, true> {
+  static constexpr int WAVES = 8, QB = 2, MIN_WAVES_PER_EU = 2, BM = 256;
+  static constexpr bool XT = false, P16 = true;
 };
 
 // LDS placement of a tile's rows.
@@ -515,6 +520,8 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
   // blocks 2c and 2c+1, keys 32g + 8c .. + 7, which is the B operand of the
   // 16x16x32 f16 product whose A operand is the widened V^T.
   int p16[QB][16];
+  const v8h ones16 = __builtin_bit_cast(v8h, (i16 == 0) ? v4i{0x3c003c00, 0x3c003c00, 0x3c003c00, 0x3c003c00}
+                                                          : v4i{0, 0, 0, 0});
   auto iteration_p16 = [&](auto last_c, auto odd_c, int j) {
     constexpr bool LAST = decltype(last_c)::value;
     constexpr bool ODD = decltype(odd_c)::value;
@@ -597,7 +604,8 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
         const int c = t >> 1;
 #pragma unroll
         for (int cb = 0; cb < C::NCB; ++cb) {
-          const v8h va = vh_operand(vhl, cb, c);
+          // hd128: block 8 is the constant ones block (row 0 = 1.0)
+          const v8h va = (D == 128 && cb == 8) ? ones16 : vh_operand(vhl, cb, c);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
             const v8h pb = __builtin_bit_cast(
@@ -854,15 +862,19 @@ hipError_t launch_shape(AttnArgs a, int total_tokens, int max_seqlen, hipStream_
 }  // namespace
 
 hipError_t launch_attn(const AttnArgs& a, int head_dim, int total_tokens, int max_seqlen, hipStream_t s) {
-  if (head_dim == 128) return launch_shape<128, false>(a, total_tokens, max_seqlen, s);
   // The wide shape once its workgroups occupy at least half of the CUs (by
   // the same upper bound on tiles the grid uses): measured faster from 144
   // workgroups on 256 CUs (L = 2304, 16 heads) up, slower at 16 (L = 256).
   const int cus = device_cus();
   if (cus == 0) return hipErrorInvalidDevice;
-  const int64_t wide_items = (int64_t)a.H * tiles_ub(Shape<72, true>::BM, total_tokens, a.nseg, max_seqlen);
-  if (2 * wide_items >= (int64_t)cus) return launch_shape<72, true>(a, total_tokens, max_seqlen, s);
-  return launch_shape<72, false>(a, total_tokens, max_seqlen, s);
+  static_assert(Shape<72, true>::BM == 256 && Shape<128, true>::BM == 256, "wide shapes");
+  const int64_t wide_items = (int64_t)a.H * tiles_ub(256, total_tokens, a.nseg, max_seqlen);
+  const bool wide = 2 * wide_items >= (int64_t)cus;
+  if (head_dim == 128)
+    return wide ? launch_shape<128, true>(a, total_tokens, max_seqlen, s)
+                : launch_shape<128, false>(a, total_tokens, max_seqlen, s);
+  return wide ? launch_shape<72, true>(a, total_tokens, max_seqlen, s)
+              : launch_shape<72, false>(a, total_tokens, max_seqlen, s);
 }
 
 }  // namespace fp8vit

@@ -225,23 +225,25 @@ def test_attention_fp8_output_small(seglens, d):
 
 
 # 64 heads make the grid wide enough (workgroups of 256 queries on at least
-# half of the CUs) for the hd72 kernel's wide shape; the ragged segments (one
+# half of the CUs) for the wide shapes; the ragged segments (one
 # token, empty, partial tiles of both shapes) then run through it. The small
 # cases above run the narrow shape.
 WIDE_SEGLENS = (1500, 1, 733, 0, 257)
 
 
-def test_attention_wide_shape_ragged():
+@pytest.mark.parametrize("d", [72, 128])
+def test_attention_wide_shape_ragged(d):
     dev = require_gpu()
     cu = make_cu_seqlens(WIDE_SEGLENS)
-    qb, kb, vb = make_qkv(91, int(cu[-1]), 64, 72)
+    qb, kb, vb = make_qkv(91 + d, int(cu[-1]), 64, d)
     check_vs_oracle(qb, kb, vb, cu, dev)
 
 
-def test_attention_wide_shape_fp8_output():
+@pytest.mark.parametrize("d", [72, 128])
+def test_attention_wide_shape_fp8_output(d):
     dev = require_gpu()
     cu = make_cu_seqlens(WIDE_SEGLENS)
-    qb, kb, vb = make_qkv(92, int(cu[-1]), 64, 72)
+    qb, kb, vb = make_qkv(92 + d, int(cu[-1]), 64, d)
     ref = oracle.pipeline.forward(qb, kb, vb, cu, "dynamic", ring=oracle.scales.AmaxRing())
     out_descale = float(np.float32(np.abs(ref.out).max() / 300.0))
     codes8, o16, codes = _run_fp8out(qb, kb, vb, cu, dev, out_descale)
