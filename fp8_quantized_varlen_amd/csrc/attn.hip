@@ -57,16 +57,19 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
 
 template <int D> struct Cfg;
-// KS/VS: LDS row strides in bytes (multiples of 16: the DMA moves 16-byte
-// chunks, so a row holds the head's D bytes followed by the first bytes of
-// the next head; those only ever meet zero Q bytes or discarded O columns).
+// KS/VS: LDS row strides of K and V tiles in bytes (multiples of 16: the DMA
+// moves 16-byte chunks, so a row holds the head's D bytes followed by the
+// first bytes of the next head; those only ever meet zero Q bytes or
+// discarded O columns). KOP: K is stored in operand order instead of rows
+// (see the K placement below; hd128: +6 %, hd72: -1.5 % for 60 % more DMA).
 // NCB: 16-column blocks of O^T including the ones column.
-// VH_COLS: V columns held in the widened (f16, transposed) tile.
 template <> struct Cfg<72> {
   static constexpr int KS = 80, VS = 80, NCB = 5, ONES_CB = 4, ONES_LANE0 = 32, VH_COLS = 80;
+  static constexpr bool KOP = false;
 };
 template <> struct Cfg<128> {
   static constexpr int KS = 144, VS = 144, NCB = 9, ONES_CB = 8, ONES_LANE0 = 0, VH_COLS = 128;
+  static constexpr bool KOP = true;
 };
 // Workgroup shapes: WAVES x QB x 16 = BM queries per workgroup, each wave
 // owning QB blocks of 16 queries that share every K and V operand it reads.
@@ -97,25 +100,34 @@ template <> struct Shape<128, true> {
   static constexpr bool XT = false, P16 = true;
 };
 
-// LDS placement of a tile's rows.
-//  K: key k sits in row 4*(k%32) + k/32, so the 16 keys of one S^T block
-//     (32a + 4t + b, a, b = 0..3) occupy 16 consecutive rows 16t..16t+15.
-//  V: key k sits in row k.
+// LDS placement of a tile. S^T block t (0..7) row i16 is key
+// 32 (i16 / 4) + 4 t + i16 % 4 (k_block_key); its A operand lane (g, i16)
+// holds d bytes 32 g .. 32 g + 31 of that key, as two 16-byte reads.
+//  K rows (KOP false): key k sits in row 4*(k%32) + k/32, so the 16 keys of
+//     one S^T block occupy 16 consecutive rows 16t..16t+15. hd72: lane groups
+//     2 and 3 both read bytes 64..95 (8 data bytes, then bytes that only meet
+//     zero Q bytes; row 127 runs into 32 zero bytes after the tile).
+//  K in operand order (KOP true): the chunk lane (g, i16) reads for (t, half h)
+//     sits at (2t + h) * 1024 + 16 * (16 g + i16), so every operand read of a
+//     wave is one contiguous kilobyte; the DMA gathers the chunks.
+//  V: key k sits in row k (VS-byte rows).
+__device__ __forceinline__ int k_block_key(int t, int i16) { return 32 * (i16 >> 2) + 4 * t + (i16 & 3); }
 __device__ __forceinline__ int k_key(int row) { return 32 * (row & 3) + (row >> 2); }
 
 template <int D, int WAVES> struct Stage {
   static constexpr int THREADS = 64 * WAVES;
-  static constexpr int KZERO = kBN * Cfg<D>::KS;                 // 32 zero bytes after the K rows
-  static constexpr int KBUF = KZERO + 32, VBUF = kBN * Cfg<D>::VS;
+  static constexpr int KZERO = kBN * Cfg<D>::KS;   // rows: 32 zero bytes after the K rows
+  static constexpr int KBUF = Cfg<D>::KOP ? 16 * 1024 : KZERO + 32, VBUF = kBN * Cfg<D>::VS;
   // Widened V, f16, in the order of the operand reads: the 16-byte chunk of
   // column 16 cb + i16 holding keys 32 g + 8 c .. + 7 sits at
   // ((4 cb + c) * 64 + 16 g + i16) * 16, so that every read (and every
   // widening store) of a wave is one contiguous kilobyte.
   static constexpr int VHBUF = (Cfg<D>::VH_COLS / 16) * 4 * 1024;
   // DMA: one wave instruction moves 64 chunks of 16 bytes (1 KB) of a tile.
-  static constexpr int NI = kBN * Cfg<D>::KS / 1024;              // instructions per K (or V) tile
-  static constexpr int NIW = (2 * NI + WAVES - 1) / WAVES;   // per wave, K and V together
-  static_assert(kBN * Cfg<D>::KS % 1024 == 0 && Cfg<D>::KS == Cfg<D>::VS, "DMA tiling");
+  static constexpr int NIK = (Cfg<D>::KOP ? 16 * 1024 : KZERO) / 1024;   // instructions per K tile
+  static constexpr int NIV = kBN * Cfg<D>::VS / 1024;            // instructions per V tile
+  static constexpr int NIW = (NIK + NIV + WAVES - 1) / WAVES;    // per wave, K and V together
+  static_assert(kBN * Cfg<D>::VS % 1024 == 0 && kBN * Cfg<D>::KS % 1024 == 0, "DMA tiling");
 };
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
@@ -127,21 +139,19 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// A operand of S^T block t: lane row i16 <-> key 32*(i16/4) + 4t + i16%4, d bytes
-// 32g..32g+31. `kl` is the lane's byte offset for t = 0 (k_lane_offset); block t
-// adds 16 rows. hd72: lane groups 2 and 3 read bytes 64..95 (8 data bytes, then
-// bytes that only meet zero bytes of the Q operand; row 127 runs into the zero
-// bytes after the tile).
+// A operand of S^T block t (see the K placement above). `kl` is the lane's
+// byte offset for t = 0 (k_lane_offset).
 template <int D>
-__device__ __forceinline__ int k_lane_offset(int g, int i16) {
+__device__ __forceinline__ int k_lane_offset(int g, int i16, int lane) {
+  if (Cfg<D>::KOP) return 16 * lane;
   const int krow = 4 * (i16 & 3) + (i16 >> 2);            // row of key 32*(i16/4) + i16%4
   return krow * Cfg<D>::KS + (D == 72 ? min(32 * g, 64) : 32 * g);
 }
 template <int D>
 __device__ __forceinline__ v8i k_operand(const lds_u8* kl, int t) {
-  const lds_u8* kp = kl + 16 * t * Cfg<D>::KS;
+  const lds_u8* kp = kl + (Cfg<D>::KOP ? 2048 * t : 16 * t * Cfg<D>::KS);
   const v4i k0 = *(const lds_v4i*)(kp);
-  const v4i k1 = *(const lds_v4i*)(kp + 16);
+  const v4i k1 = *(const lds_v4i*)(kp + (Cfg<D>::KOP ? 1024 : 16));
   return __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
@@ -228,7 +238,7 @@ __device__ __forceinline__ int2 probs_to_fp8(const v4f& s, float c, float nb, in
 
 // This wave's share of the DMA of one K tile (koff: its global byte offset)
 // into kdst and, with_v, one V tile into vdst. Instruction i = wave + WAVES*n
-// of a tile moves chunks 64*i .. 64*i+63 of K (i < NI) or of V (NI <= i < 2 NI);
+// of a tile moves LDS kilobyte i of K (i < NIK) or kilobyte i - NIK of V;
 // dma_off[n] holds the lane's global offset for tile 0.
 template <int D, int WAVES>
 __device__ __forceinline__ void dma_issue(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
@@ -238,10 +248,10 @@ __device__ __forceinline__ void dma_issue(__amdgpu_buffer_rsrc_t krs, __amdgpu_b
 #pragma unroll
   for (int n = 0; n < S::NIW; ++n) {
     const int i = wave + WAVES * n;   // wave-uniform
-    if (i < S::NI) {
+    if (i < S::NIK) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kdst + 1024 * i), 16, dma_off[n] + koff, 0, 0, 0);
-    } else if (i < 2 * S::NI && with_v) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vdst + 1024 * (i - S::NI)), 16, dma_off[n] + voff, 0,
+    } else if (i < S::NIK + S::NIV && with_v) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vdst + 1024 * (i - S::NIK)), 16, dma_off[n] + voff, 0,
                                                0, 0);
     }
   }
@@ -298,18 +308,25 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.v8 + seg_off), (short)0, (int)(a.tensor_bytes - seg_off), kRsrcWord3);
   // This wave's DMA instructions n = 0..NIW-1 are instruction i = wave + WAVES*n
-  // of the tile (K for i < NI, V after). Lane l of instruction ii moves the
-  // 16-byte chunk c = 64*ii + l of the tile's LDS image: row c / (KS/16),
-  // piece c % (KS/16). dma_off: its byte offset in global memory for tile 0.
+  // of the tile (K for i < NIK, V after). dma_off: lane l's byte offset in
+  // global memory for tile 0. K in operand order, instruction i = 2t + h: the
+  // chunk of lane (g, i16) in the K placement above. Rows (K or V),
+  // instruction ii: chunk c = 64*ii + l of the image, row c / (S/16), piece
+  // c % (S/16) for the row stride S.
   uint32_t dma_off[S::NIW];
 #pragma unroll
   for (int n = 0; n < S::NIW; ++n) {
     const int i = wave + SH::WAVES * n;
-    const int ii = i < S::NI ? i : i - S::NI;
-    const int c = 64 * ii + lane;
-    const int row = c / (C::KS / 16), piece = c % (C::KS / 16);
-    const int key = i < S::NI ? k_key(row) : row;
-    dma_off[n] = (uint32_t)key * row_stride + 16u * (uint32_t)piece;
+    if (i < S::NIK && C::KOP) {
+      dma_off[n] = (uint32_t)k_block_key(i >> 1, i16) * row_stride + 32u * g + 16u * (i & 1);
+    } else if (i < S::NIK) {
+      const int c = 64 * i + lane;
+      const int row = c / (C::KS / 16), piece = c % (C::KS / 16);
+      dma_off[n] = (uint32_t)k_key(row) * row_stride + 16u * (uint32_t)piece;
+    } else {
+      const int c = 64 * (i - S::NIK) + lane;
+      dma_off[n] = (uint32_t)(c / (C::VS / 16)) * row_stride + 16u * (uint32_t)(c % (C::VS / 16));
+    }
   }
   // Issue this wave's DMA of K tile tk into kdst and (with_v) V tile tv into vdst.
   auto dma_tiles = [&](int tk, uint8_t* kdst, int tv, uint8_t* vdst, bool with_v) {
@@ -319,9 +336,11 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
 
   dma_tiles(0, k_lds0, 0, v_lds0, !SH::XT);    // K(0), and V(0) unless iteration 0 loads it
   dma_tiles(1, k_lds1, 1, v_lds1, SH::P16);    // K(1), and V(1) for the widening pipeline
-  // Zero the 32 bytes after each K tile (read only against zero Q bytes).
-  for (int r = tid; r < 2 * 4; r += S::THREADS)
-    *reinterpret_cast<uint2*>((r < 4 ? k_lds0 : k_lds1) + S::KZERO + 8 * (r % 4)) = make_uint2(0u, 0u);
+  if constexpr (!C::KOP) {
+    // Zero the 32 bytes after each K tile (read only against zero Q bytes).
+    for (int r = tid; r < 2 * 4; r += S::THREADS)
+      *reinterpret_cast<uint2*>((r < 4 ? k_lds0 : k_lds1) + S::KZERO + 8 * (r % 4)) = make_uint2(0u, 0u);
+  }
 
   const float dq = a.st->descale_used[0], dk = a.st->descale_used[1], dv = a.st->descale_used[2];
   const float cexp = a.softmax_scale * dq * dk * kLog2e;   // raw score -> log2 units (> 0)
@@ -367,7 +386,7 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's DMA of K(0), K(1), V(0)
   __syncthreads();
-  const int kl_lane = k_lane_offset<D>(g, i16);
+  const int kl_lane = k_lane_offset<D>(g, i16, lane);
   const int vl_lane = v_lane_offset<D>(g, i16);
   const int vhl_lane = 16 * lane;
   if constexpr (SH::P16) widen_v<D, SH::WAVES>(v_lds0, vh_lds0, wave, g, i16, vl_lane);   // V(0)
