@@ -32,7 +32,9 @@
 //    relative error to O). The wide shapes round it once to f16 and run P.V
 //    on the f16 MFMA against V widened (exactly) into an f16 copy in LDS; the
 //    narrow shapes give the FP8 MFMA two e4m3 terms, hi = e4m3(P~) and
-//    lo = e4m3(P~ - hi).
+//    lo = e4m3(P~ - hi). The wide hd72 kernel (attn_w32_kernel) works on
+//    32x32 MFMA blocks, so that d = 72 costs 80 columns of S = K Q^T work
+//    instead of 128.
 //  * Work items are (head, query tile); consecutive items of one head are
 //    mapped to the same XCD so that K/V re-reads hit that XCD's L2.
 #include <type_traits>
@@ -71,12 +73,12 @@ template <> struct Cfg<128> {
   static constexpr int KS = 144, VS = 144, NCB = 9, ONES_CB = 8, ONES_LANE0 = 0, VH_COLS = 128;
   static constexpr bool KOP = true;
 };
-// Workgroup shapes: WAVES x QB x 16 = BM queries per workgroup, each wave
-// owning QB blocks of 16 queries that share every K and V operand it reads.
-// The wide shapes (two query blocks per wave, 256 queries per workgroup,
-// 2 waves per SIMD) halve the LDS reads and the K/V staging per query; they
-// are used unless the problem is too small to spread their workgroups over
-// the chip.
+// Workgroup shapes of attn_kernel: WAVES x QB x 16 = BM queries per
+// workgroup, each wave owning QB blocks of 16 queries that share every K and
+// V operand it reads. The wide shapes (256 queries per workgroup, 2 waves per
+// SIMD: hd128 with two query blocks per wave here, hd72 in attn_w32_kernel
+// below) halve the LDS reads and the K/V staging per query; they are used
+// unless the problem is too small to spread their workgroups over the chip.
 template <int D, bool WIDE> struct Shape;
 // XT: the P.V products of tile j-1 run interleaved with the softmax of tile
 // j (a second P register set) instead of as a burst at the end of tile j-1.
@@ -86,10 +88,6 @@ template <int D, bool WIDE> struct Shape;
 template <> struct Shape<72, false> {
   static constexpr int WAVES = 8, QB = 1, MIN_WAVES_PER_EU = 4, BM = 128;
   static constexpr bool XT = false, P16 = false;
-};
-template <> struct Shape<72, true> {
-  static constexpr int WAVES = 8, QB = 2, MIN_WAVES_PER_EU = 2, BM = 256;
-  static constexpr bool XT = false, P16 = true;
 };
 template <> struct Shape<128, false> {
   static constexpr int WAVES = 8, QB = 1, MIN_WAVES_PER_EU = 2, BM = 128;
@@ -842,6 +840,323 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
   }
 }
 
+// ---------------------------------------------------------------------------
+// hd72, 256 queries per workgroup, on 32x32 MFMA blocks.
+//
+// Each wave owns 32 queries; lane l works on query l % 32, lane half
+// hf = l / 32. S^T = K Q^T comes in four 32-key blocks u per 128-key tile,
+// each from one v_mfma_f32_32x32x64_f8f6f4 (d bytes 0..63) and one
+// v_mfma_f32_32x32x16_fp8_fp8 (d bytes 64..79; Q bytes 72..79 are zero), so
+// d = 72 costs 80 columns of MFMA work instead of 128. Output layout of a
+// 32x32 block: lane l, register r holds row 8 (r/4) + 4 hf + r % 4, column
+// l % 32. P~ goes as f16 into O^T += V^T P^T on v_mfma_f32_32x32x16_f16,
+// O^T in three 32-row blocks (d 0..95; row 72 is the row-sum column).
+//
+// K in LDS, per 32-key block u at u * 2560: bytes 0..2047 hold the A operand
+// of the 32x32x64 product, half hh of lane l at hh * 1024 + 16 l (key
+// 32u + l%32, d bytes 32 (l/32) + 16 hh); bytes 2048..2559 hold d bytes 64..79
+// of key 32u + m at 16 m (lane l reads 8 bytes at 16 (l%32) + 8 (l/32)).
+// The DMA gathers these 16-byte chunks: 10 KB per tile, as for rows.
+//
+// 16-key chunk (u, qq) of the P.V product: B operand lane l holds the f16 P~
+// of S registers 8qq..8qq+7 of block u, i.e. keys 32u + 16qq + 4 hf + e for
+// e in {0,1,2,3,8,9,10,11}; the widened V^T holds, for d row 32 db + l%32,
+// the same keys in the same order at ((8 db + 2u + qq) * 64 + l) * 16, so
+// every operand read and every widening store is contiguous.
+// ---------------------------------------------------------------------------
+namespace w32 {
+constexpr int WAVES = 8, BM = 256, KBUF = 10240, VBUF = kBN * 80, VHBUF = 3 * 8 * 1024;
+constexpr int NIW = (10 + 10 + WAVES - 1) / WAVES;
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) long lds_i64;
+
+__device__ __forceinline__ v16f mfma64(const v8i& a, const v8i& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+__device__ __forceinline__ v16f mfma16(long a, long b, const v16f& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a, b, c, 0, 0, 0);
+}
+
+// One wave's share of widening the e4m3 V tile (80-byte rows) into the f16
+// operand layout above. Unit i = (16-column block cb, 8-key step sidx): lane
+// (g, i16) reads keys 32g + 8 sidx .. + 7 of column c = 16 cb + i16; keys
+// e = 0..3 go to lane half 0 and e = 4..7 to half 1 of chunk (db = c/32, u = g,
+// qq = sidx/2), as its 8-byte half sidx % 2. Column 72 is written as 1.0,
+// 73..79 as 0.
+__device__ __forceinline__ void widen(const uint8_t* v8, uint8_t* vh, int wave, int g, int i16, int vl_lane) {
+#pragma unroll
+  for (int n = 0; n < (20 + WAVES - 1) / WAVES; ++n) {
+    const int i = wave + WAVES * n;
+    if (i < 20) {
+      const int cb = i >> 2, sidx = i & 3;
+      const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (lds_v2i*)((const lds_u8*)v8 + vl_lane + 8 * sidx * 80 + 16 * cb));
+      const int c = 16 * cb + i16;
+      v2i lo, hi;   // keys e = 0..3 and 4..7 as f16
+      lo[0] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[0], 1.0f, false));
+      lo[1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[0], 1.0f, true));
+      hi[0] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[1], 1.0f, false));
+      hi[1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[1], 1.0f, true));
+      if (c >= 72) {
+        const int f = c == 72 ? 0x3c003c00 : 0;
+        lo = v2i{f, f};
+        hi = v2i{f, f};
+      }
+      const int chunk = 8 * (c >> 5) + 2 * g + (sidx >> 1);
+      lds_u8* base = (lds_u8*)vh + chunk * 1024 + 8 * (sidx & 1);
+      *(lds_v2i*)(base + 16 * (c & 31)) = lo;
+      *(lds_v2i*)(base + 16 * (32 + (c & 31))) = hi;
+    }
+  }
+}
+}  // namespace w32
+
+template <bool OUT8>
+__global__ __launch_bounds__(64 * w32::WAVES) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_w32_kernel(AttnArgs a) {
+  using namespace w32;
+  constexpr int D = 72;
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[KBUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[KBUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[VBUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[VBUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t vh_lds0[VHBUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t vh_lds1[VHBUF];
+
+  // ---- work item: XCD-grouped (head, query tile) -> segment by prefix scan ----
+  const int G = gridDim.x;
+  const int w = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const int h = w / a.ntiles_ub;
+  int tile = w - h * a.ntiles_ub;
+  if (h >= a.H) return;
+  int s0 = 0, L = -1;
+  for (int i = 0; i < a.nseg; ++i) {
+    const int b0 = a.cu[i], b1 = a.cu[i + 1];
+    const int n = (b1 - b0 + BM - 1) / BM;
+    if (tile < n) { s0 = b0; L = b1 - b0; break; }
+    tile -= n;
+  }
+  if (L <= 0) return;
+  const int q0 = tile * BM;
+  const int ntiles = (L + kBN - 1) / kBN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, i16 = lane & 15;
+  const int hf = lane >> 5, l32 = lane & 31;
+
+  // ---- DMA geometry (chunks as described above) ----
+  const uint32_t row_stride = (uint32_t)a.H * D;
+  const uint32_t seg_off = ((uint32_t)s0 * (uint32_t)a.H + (uint32_t)h) * D;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.k8 + seg_off), (short)0, (int)(a.tensor_bytes - seg_off), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.v8 + seg_off), (short)0, (int)(a.tensor_bytes - seg_off), kRsrcWord3);
+  uint32_t dma_off[NIW];
+#pragma unroll
+  for (int n = 0; n < NIW; ++n) {
+    const int i = wave + WAVES * n;
+    if (i < 10) {
+      const int c = 64 * i + lane, u = c / 160, r = c % 160;
+      if (r < 128) {
+        const int hh = r >> 6, ln = r & 63;
+        dma_off[n] = (uint32_t)(32 * u + (ln & 31)) * row_stride + 32u * (uint32_t)(ln >> 5) + 16u * hh;
+      } else {
+        dma_off[n] = (uint32_t)(32 * u + (r - 128)) * row_stride + 64u;
+      }
+    } else {
+      const int c = 64 * (i - 10) + lane;
+      dma_off[n] = (uint32_t)(c / 5) * row_stride + 16u * (uint32_t)(c % 5);
+    }
+  }
+  auto dma_tiles = [&](int tk, uint8_t* kdst, int tv, uint8_t* vdst, bool with_v) {
+    dma_issue<D, WAVES>(krs, vrs, dma_off, wave, (uint32_t)tk * kBN * row_stride, kdst,
+                        (uint32_t)tv * kBN * row_stride, vdst, with_v);
+  };
+  dma_tiles(0, k_lds0, 0, v_lds0, true);
+  dma_tiles(1, k_lds1, 1, v_lds1, true);
+  // Rows 80..95 of the widened V^T (no V columns) stay zero: in each buffer,
+  // chunks 16..23 (block db = 2), lanes with l % 32 >= 16.
+  for (int r = tid; r < 2 * 256; r += 64 * WAVES) {
+    const int idx = r & 255, ln = 32 * ((idx >> 4) & 1) + 16 + (idx & 15);
+    uint8_t* vb = (r < 256 ? vh_lds0 : vh_lds1) + (16 + (idx >> 5)) * 1024 + 16 * ln;
+    *reinterpret_cast<uint4*>(vb) = make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  const float dq = a.st->descale_used[0], dk = a.st->descale_used[1], dv = a.st->descale_used[2];
+  const float cexp = a.softmax_scale * dq * dk * kLog2e;
+
+  // ---- Q operands: lane l: query l%32, d bytes 32 hf .. + 31, and 64 + 8 hf .. + 7 ----
+  v8i qa = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  long qbv = 0;
+  {
+    const int qr = q0 + wave * 32 + l32;
+    if (qr < L) {
+      const uint8_t* src = a.q8 + ((int64_t)(s0 + qr) * a.H + h) * D;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint2 u2 = *reinterpret_cast<const uint2*>(src + 32 * hf + 8 * j);
+        qa[2 * j] = (int)u2.x;
+        qa[2 * j + 1] = (int)u2.y;
+      }
+      if (hf == 0) qbv = *reinterpret_cast<const long*>(src + 64);
+    }
+  }
+
+  v16f o[3];
+#pragma unroll
+  for (int db = 0; db < 3; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  float mref = -INFINITY, thr = -INFINITY;
+  v16f zero16;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) zero16[r] = 0.f;
+
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's DMA of K(0), K(1), V(0), V(1)
+  __syncthreads();
+  const int vl_lane = v_lane_offset<D>(g, i16);
+  widen(v_lds0, vh_lds0, wave, g, i16, vl_lane);      // V(0)
+
+  const int ka_lane = 16 * lane, kb_lane = 2048 + 16 * l32 + 8 * hf;
+  auto k_a = [&](const lds_u8* kb, int u) -> v8i {
+    const v4i x0 = *(const lds_v4i*)(kb + u * 2560 + ka_lane);
+    const v4i x1 = *(const lds_v4i*)(kb + u * 2560 + ka_lane + 1024);
+    return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto k_b = [&](const lds_u8* kb, int u) -> long { return *(const lds_i64*)(kb + u * 2560 + kb_lane); };
+
+  // S(0)
+  v16f sc[4];
+  {
+    const lds_u8* kb = (const lds_u8*)k_lds0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      sc[u] = mfma64(k_a(kb, u), qa, zero16);
+      sc[u] = mfma16(k_b(kb, u), qbv, sc[u]);
+    }
+  }
+
+  int pf[4][8];   // f16 P~ of block u: dwords 4qq .. 4qq+3 are chunk (u, qq)
+  auto iteration = [&](auto last_c, auto odd_c, int j) {
+    constexpr bool LAST = decltype(last_c)::value;
+    constexpr bool ODD = decltype(odd_c)::value;
+    uint8_t* const k_fill = ODD ? k_lds1 : k_lds0;          // K(j+2)
+    uint8_t* const v_fill = ODD ? v_lds1 : v_lds0;          // e4m3 V(j+2)
+    const uint8_t* const v_conv = ODD ? v_lds0 : v_lds1;    // e4m3 V(j+1)
+    uint8_t* const vh_fill = ODD ? vh_lds0 : vh_lds1;       // f16 V(j+1)
+    const uint8_t* const k_read = ODD ? k_lds0 : k_lds1;    // K(j+1)
+    const uint8_t* const vh_read = ODD ? vh_lds1 : vh_lds0; // f16 V(j)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    dma_tiles(j + 2, k_fill, j + 2, v_fill, true);
+    if (!LAST) widen(v_conv, vh_fill, wave, g, i16, vl_lane);
+    if (LAST) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sc[u][r] = (j * kBN + 32 * u + 8 * (r >> 2) + 4 * hf + (r & 3) >= L) ? -INFINITY : sc[u][r];
+    }
+    // Lazy reference max (see the narrow kernels): the row of query l%32 is
+    // split over lanes l and l ^ 32.
+    float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; r += 8) {
+        m0 = fmaxf(fmaxf(fmaxf(fmaxf(m0, sc[u][r]), sc[u][r + 1]), sc[u][r + 2]), sc[u][r + 3]);
+        m1 = fmaxf(fmaxf(fmaxf(fmaxf(m1, sc[u][r + 4]), sc[u][r + 5]), sc[u][r + 6]), sc[u][r + 7]);
+      }
+    const float lm = fmaxf(m0, m1);
+    if (__ballot(lm > thr) != 0ull) {
+      const float m = fmaxf(lm, __shfl_xor(lm, 32, 64));
+      const float mn = fmaxf(mref, m * cexp);
+      const float alpha = __builtin_amdgcn_exp2f(mref - mn);
+      mref = mn;
+      thr = (mn + kLazy) / cexp;
+#pragma unroll
+      for (int db = 0; db < 3; ++db) o[db] *= alpha;
+    }
+    const float nb = kExpBias - mref;
+
+    uint32_t kbase = 0, vbase = (uint32_t)(16 * lane);
+    asm volatile("" : "+v"(kbase), "+v"(vbase));
+    const lds_u8* kb = (const lds_u8*)k_read + kbase;
+    const lds_u8* vhl = (const lds_u8*)vh_read + vbase;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[u][r], cexp, nb));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[u][r + 1], cexp, nb));
+        pf[u][r >> 1] = __builtin_bit_cast(int, (v2h){(_Float16)p0, (_Float16)p1});
+      }
+      if (!LAST) {
+        sc[u] = mfma64(k_a(kb, u), qa, zero16);
+        sc[u] = mfma16(k_b(kb, u), qbv, sc[u]);
+      }
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        const v8h pb = __builtin_bit_cast(v8h, v4i{pf[u][4 * qq], pf[u][4 * qq + 1], pf[u][4 * qq + 2], pf[u][4 * qq + 3]});
+#pragma unroll
+        for (int db = 0; db < 3; ++db) {
+          const v8h va = *(const lds_v8h*)(vhl + (8 * db + 2 * u + qq) * 1024);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb, o[db], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);   // keep each u step's exps ahead of its own MFMAs
+    }
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  int j = 0;
+  for (; j + 2 < ntiles; j += 2) {
+    iteration(F_{}, F_{}, j);
+    iteration(F_{}, T_{}, j + 1);
+  }
+  if (j + 1 < ntiles) {
+    iteration(F_{}, F_{}, j);
+    iteration(T_{}, T_{}, j + 1);
+  } else {
+    iteration(T_{}, F_{}, j);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no DMA in flight past the loop
+
+  // ---- epilogue: row sum = O^T row 72 (block 2, register 4 of half 0) ----
+  double out_rcp = 0.0;
+  if (OUT8) out_rcp = 1.0 / (double)(*a.out_descale);
+  const float lsum = __shfl(o[2][4], l32, 64);
+  const float f = dv / lsum;
+  const int qr = q0 + wave * 32 + l32;
+  if (qr < L) {
+    const int64_t row = (int64_t)(s0 + qr) * a.ld_out + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < 3; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int col = 32 * db + 8 * i + 4 * hf;
+        if (col + 4 <= D) {
+          const v4f x = v4f{o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]} * f;
+          if (OUT8) {
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              y[e] = __builtin_amdgcn_fmed3f((float)((double)x[e] * out_rcp), -kFp8Max, kFp8Max);
+            int wv = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+            wv = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], wv, true);
+            *reinterpret_cast<int*>(a.out8 + row + col) = wv;
+          } else {
+            uint2 pk;
+            pk.x = bf16_rne(x[0]) | (bf16_rne(x[1]) << 16);
+            pk.y = bf16_rne(x[2]) | (bf16_rne(x[3]) << 16);
+            *reinterpret_cast<uint2*>(a.out + row + col) = pk;
+          }
+        }
+      }
+  }
+}
+
 int attn_block_m(int head_dim) { return head_dim == 72 ? Shape<72, false>::BM : Shape<128, false>::BM; }
 
 namespace {
@@ -878,6 +1193,18 @@ hipError_t launch_shape(AttnArgs a, int total_tokens, int max_seqlen, hipStream_
     hipLaunchKernelGGL((attn_kernel<D, false, WIDE>), dim3((unsigned)grid), block, 0, s, a);
   return hipGetLastError();
 }
+hipError_t launch_w32(AttnArgs a, int total_tokens, int max_seqlen, hipStream_t s) {
+  a.ntiles_ub = (int32_t)tiles_ub(w32::BM, total_tokens, a.nseg, max_seqlen);
+  const int64_t items = (int64_t)a.H * a.ntiles_ub;
+  const int64_t grid = ((items + 7) / 8) * 8;
+  if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const dim3 block(64 * w32::WAVES);
+  if (a.out8 != nullptr)
+    hipLaunchKernelGGL(attn_w32_kernel<true>, dim3((unsigned)grid), block, 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_w32_kernel<false>, dim3((unsigned)grid), block, 0, s, a);
+  return hipGetLastError();
+}
 }  // namespace
 
 hipError_t launch_attn(const AttnArgs& a, int head_dim, int total_tokens, int max_seqlen, hipStream_t s) {
@@ -886,14 +1213,13 @@ hipError_t launch_attn(const AttnArgs& a, int head_dim, int total_tokens, int ma
   // workgroups on 256 CUs (L = 2304, 16 heads) up, slower at 16 (L = 256).
   const int cus = device_cus();
   if (cus == 0) return hipErrorInvalidDevice;
-  static_assert(Shape<72, true>::BM == 256 && Shape<128, true>::BM == 256, "wide shapes");
+  static_assert(w32::BM == 256 && Shape<128, true>::BM == 256, "wide shapes");
   const int64_t wide_items = (int64_t)a.H * tiles_ub(256, total_tokens, a.nseg, max_seqlen);
   const bool wide = 2 * wide_items >= (int64_t)cus;
   if (head_dim == 128)
     return wide ? launch_shape<128, true>(a, total_tokens, max_seqlen, s)
                 : launch_shape<128, false>(a, total_tokens, max_seqlen, s);
-  return wide ? launch_shape<72, true>(a, total_tokens, max_seqlen, s)
-              : launch_shape<72, false>(a, total_tokens, max_seqlen, s);
+  return wide ? launch_w32(a, total_tokens, max_seqlen, s) : launch_shape<72, false>(a, total_tokens, max_seqlen, s);
 }
 
 }  // namespace fp8vit
