@@ -66,11 +66,18 @@ def test_attention_custom_softmax_scale_and_static():
     check_vs_oracle(qb, kb, vb, cu, dev, mode="static", static_values=[4.0, 5.0, 6.0])
 
 
-def test_attention_invariants():
+# (heads, head_dim): 2 heads run the narrow shapes; 64 heads give enough work
+# items for the wide ones (256 queries per workgroup; the 32x32-block kernel at
+# head_dim 72).
+SHAPE_CASES = [(2, 72), (2, 128), (64, 72), (64, 128)]
+
+
+@pytest.mark.parametrize("H,d", SHAPE_CASES)
+def test_attention_invariants(H, d):
     dev = require_gpu()
     seglens = (130, 1, 0, 257, 64)
     cu = make_cu_seqlens(seglens)
-    T, H, d = int(cu[-1]), 2, 72
+    T = int(cu[-1])
     qb, kb, vb = make_qkv(41, T, H, d)
     o, codes, st = run_gpu(qb, kb, vb, cu, dev)
     # run-to-run determinism (no float atomics in the accumulation)
@@ -102,11 +109,12 @@ def test_attention_invariants():
     assert np.array_equal(o_2, 2 * o)
 
 
-def test_attention_equal_keys_give_segment_mean():
+@pytest.mark.parametrize("H,d", SHAPE_CASES)
+def test_attention_equal_keys_give_segment_mean(H, d):
     dev = require_gpu()
     seglens = (50, 200)
     cu = make_cu_seqlens(seglens)
-    qb, kb, vb = make_qkv(5, 250, 2, 72)
+    qb, kb, vb = make_qkv(5, 250, H, d)
     kb = kb.copy()
     kb[:50] = kb[0]
     kb[50:] = kb[50]
