@@ -64,9 +64,11 @@ template <int D> struct Cfg;
 // first bytes of the next head; those only ever meet zero Q bytes or
 // discarded O columns). KOP: K is stored in operand order instead of rows
 // (see the K placement below; hd128: +6 %, hd72: -1.5 % for 60 % more DMA).
-// NCB: 16-column blocks of O^T including the ones column.
+// NCB: 16-column blocks of O^T including the ones column. VH_COLS: columns of
+// the f16 copy of V (the wide hd128 shape; no hd72 shape of attn_kernel
+// widens V).
 template <> struct Cfg<72> {
-  static constexpr int KS = 80, VS = 80, NCB = 5, ONES_CB = 4, ONES_LANE0 = 32, VH_COLS = 80;
+  static constexpr int KS = 80, VS = 80, NCB = 5, ONES_CB = 4, ONES_LANE0 = 32, VH_COLS = 0;
   static constexpr bool KOP = false;
 };
 template <> struct Cfg<128> {
@@ -178,12 +180,13 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v8h lds_v8h;
 
 // One wave's share of widening an e4m3 V tile (row-major, VS-byte rows) into
-// the f16 tile. Unit i = (column block cb, 8-key step sidx) is one
+// the f16 tile of the wide hd128 shape (the wide hd72 kernel has its own
+// layout, attn_w32_kernel). Unit i = (column block cb, 8-key step sidx) is one
 // byte-transposing read: lane (g, i16) gets keys 32g + 8 sidx .. + 7 of
 // column 16 cb + i16, converts them and stores its 16 B at 1024 i + 16 lane.
-// hd72: column 72 becomes 1.0 (the row-sum column) and columns 73..79 zero.
 template <int D, int WAVES>
 __device__ __forceinline__ void widen_v(const uint8_t* v8, uint8_t* vh, int wave, int g, int i16, int vl_lane) {
+  static_assert(D == 128, "the f16 P.V path of attn_kernel is the wide hd128 shape");
   constexpr int NU = (Cfg<D>::VH_COLS / 16) * 4;
 #pragma unroll
   for (int n = 0; n < (NU + WAVES - 1) / WAVES; ++n) {
@@ -192,16 +195,11 @@ __device__ __forceinline__ void widen_v(const uint8_t* v8, uint8_t* vh, int wave
       const int cb = i >> 2, sidx = i & 3;
       const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
           (lds_v2i*)((const lds_u8*)v8 + vl_lane + 8 * sidx * Cfg<D>::VS + 16 * cb));
-      const int col = 16 * cb + i16;
       v4i y;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         y[2 * h] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[h], 1.0f, false));
         y[2 * h + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[h], 1.0f, true));
-      }
-      if (D == 72 && col >= 72) {
-        const int f = col == 72 ? 0x3c003c00 : 0;
-        y = v4i{f, f, f, f};
       }
       *(lds_v4i*)((lds_u8*)vh + 1024 * i + 16 * (16 * g + i16)) = y;
     }
