@@ -109,6 +109,33 @@ def test_attention_invariants(H, d):
     assert np.array_equal(o_2, 2 * o)
 
 
+@pytest.mark.parametrize("direction", ["growing", "falling"])
+@pytest.mark.parametrize("H,d", SHAPE_CASES)
+def test_attention_monotone_scores(H, d, direction):
+    """Scores that grow along the keys by ~3 log2 units per 128-key tile move
+    the lazy reference max (threshold 1.75) in nearly every tile, so O and
+    the row sum are rescaled again and again; falling scores never move it
+    after the first tile and drive the later probabilities toward underflow."""
+    dev = require_gpu()
+    seglens = (900, 300, 1)
+    cu = make_cu_seqlens(seglens)
+    T = int(cu[-1])
+    rng = np.random.Generator(np.random.PCG64(91))
+    u = rng.standard_normal(d).astype(np.float32)
+    u /= np.linalg.norm(u)
+    pos = np.zeros(T, np.float32)   # key position along its segment, reversed when falling
+    for s0, s1 in zip(cu[:-1], cu[1:]):
+        j = np.arange(s1 - s0, dtype=np.float32)
+        pos[s0:s1] = j if direction == "growing" else (s1 - s0 - 1) - j
+    # q.k / sqrt(d) * log2(e) = 3 * pos / 128 with q ~ 8u and k ~ c pos u
+    c = 3.0 / 128.0 / np.log2(np.e) * np.sqrt(d) / 8.0
+    q = 8.0 * u + 0.2 * rng.standard_normal((T, H, d), dtype=np.float32)
+    k = c * pos[:, None, None] * u + 0.2 * rng.standard_normal((T, H, d), dtype=np.float32)
+    v = rng.standard_normal((T, H, d), dtype=np.float32)
+    qb, kb, vb = (f32_to_bf16_bits(x) for x in (q, k, v))
+    check_vs_oracle(qb, kb, vb, cu, dev)
+
+
 @pytest.mark.parametrize("H,d", SHAPE_CASES)
 def test_attention_equal_keys_give_segment_mean(H, d):
     dev = require_gpu()
