@@ -319,3 +319,39 @@ def test_attention_fp8_output_full_size_sampled():
     got16 = np.stack([o16[t, h] for t, h in rows])
     _check_fp8_output(got8, got16, ref, out_descale, vmax_of(vb))
     assert not np.any((codes8 & 0x7F) == 0x7F)
+
+
+@pytest.mark.parametrize("out_type", ["bf16", "fp8"])
+@pytest.mark.parametrize("H,d", SHAPE_CASES)
+def test_attention_writes_only_its_output(H, d, out_type):
+    """The output is a view inside a larger canary-filled buffer: guard rows
+    above and below, a padded token stride (ld_out = H*d + 40) and 16 elements
+    of offset. The view must equal the contiguous run bitwise and every element
+    outside it must keep the canary."""
+    dev = require_gpu()
+    seglens = (130, 1, 0, 257, 64)
+    cu = make_cu_seqlens(seglens)
+    T = int(cu[-1])
+    qb, kb, vb = make_qkv(57, T, H, d)
+    st = fv.new_state(dev)
+    q8, k8, v8 = fv.quantize_qkv(to_dev(qb, dev), to_dev(kb, dev), to_dev(vb, dev), st, "dynamic")
+    cu_d = torch.from_numpy(np.asarray(cu, np.int32)).to(dev)
+    G, off, ld = 3, 16, H * d + 40
+    if out_type == "bf16":
+        big = torch.full((T + 2 * G, ld), -7.0, dtype=torch.bfloat16, device=dev)
+        view = big[G:G + T, off:off + H * d].unflatten(1, (H, d))
+        fv.attn_varlen(q8, k8, v8, cu_d, max(seglens), st, out=view)
+        ref = fv.attn_varlen(q8, k8, v8, cu_d, max(seglens), st)
+    else:
+        s_d = torch.tensor([0.01], dtype=torch.float32, device=dev)
+        big = torch.full((T + 2 * G, ld), 0x5A, dtype=torch.uint8, device=dev)
+        view = big[G:G + T, off:off + H * d].unflatten(1, (H, d))
+        fv.attn_varlen_fp8out(q8, k8, v8, cu_d, max(seglens), st, s_d, out=view)
+        ref = fv.attn_varlen_fp8out(q8, k8, v8, cu_d, max(seglens), st, s_d)
+    torch.cuda.synchronize()
+    assert view.stride() == (ld, d, 1)
+    assert torch.equal(view, ref)
+    mask = torch.ones_like(big, dtype=torch.bool)
+    mask[G:G + T, off:off + H * d] = False
+    canary = -7.0 if out_type == "bf16" else 0x5A
+    assert torch.all(big[mask] == canary), "writes outside the output view"

@@ -174,3 +174,31 @@ def test_quantize_full_size_workloads(name):
     assert np.array_equal(f32bits(fv.state_read(st)["descale_used"]), f32bits(ds))
     for c, r in zip((q8, k8, v8), codes):
         assert np.array_equal(codes_np(c), r)
+
+
+def test_quantize_writes_only_its_outputs():
+    """Each code tensor is a view inside a larger buffer filled with a canary:
+    the views hold the same codes as a contiguous run and nothing else changes."""
+    dev = require_gpu()
+    T, H, d = 777, 3, 72
+    qb, kb, vb = make_qkv(61, T, H, d)
+    q, k, v = (to_dev(x, dev) for x in (qb, kb, vb))
+    n = T * H * d
+    outs, bigs = [], []
+    for x in range(3):
+        big = torch.full((n + 4096,), 0xA5, dtype=torch.uint8, device=dev)
+        bigs.append(big)
+        outs.append(big[2048:2048 + n].view(T, H, d))
+    for mode in ("dynamic", "static"):
+        st = fv.new_state(dev)
+        if mode == "static":
+            fv.state_set_static(st, [3.0, 4.0, 5.0])
+        fv.quantize_qkv(q, k, v, st, mode, out=tuple(outs))
+        st2 = fv.new_state(dev)
+        if mode == "static":
+            fv.state_set_static(st2, [3.0, 4.0, 5.0])
+        ref = fv.quantize_qkv(q, k, v, st2, mode)
+        torch.cuda.synchronize()
+        for x in range(3):
+            assert torch.equal(outs[x], ref[x])
+            assert torch.all(bigs[x][:2048] == 0xA5) and torch.all(bigs[x][2048 + n:] == 0xA5)
