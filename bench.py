@@ -327,6 +327,7 @@ def main():
     assert not torch.isnan(out).any().item()
     state = fv.state_read(st)
 
+    kname = attn_kernel_name(w, dev, args.out == "fp8")
     value = w.flops / (ms_step * 1e-3) / 1e12
     attn_tflops = w.flops / (attn_ms * 1e-3) / 1e12
     quant_bytes = 3 * T * H * d * 3
@@ -341,7 +342,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(value / PAGE_MI300X_TFLOPS[w.name], 3) if w.name in PAGE_MI300X_TFLOPS else None,
-        "dtype": "fp8e4m3",
+        # S = Q K^T on the FP8 MFMA; P.V on the f16 MFMA in the wide kernels,
+        # on the FP8 MFMA (two e4m3 terms of P) in the narrow ones
+        "dtype": "fp8e4m3+f16" if kname.startswith("attn_w32") or kname.endswith(", true>") else "fp8e4m3",
         "data": "synthetic",
         "config": {"workload": w.name, "segments": list(w.seglens), "heads": H, "head_dim": d, "output": args.out,
                    "scaling": w.mode + (" (1.5 x calibrated)" if w.mode == "static" else " (16-slot ring)"),
@@ -354,7 +357,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4),
                      "traffic": attn_traffic(w.name, d),
-                     "kernel": attn_kernel_name(w, dev, args.out == "fp8")},
+                     "kernel": kname},
         "descale_used": state["descale_used"],
         **({"graph": {"ms_per_step": round(graph_ms, 4),
                       "value": round(w.flops / (graph_ms * 1e-3) / 1e12, 2)}} if graph_ms else {}),
