@@ -60,6 +60,8 @@ def test_argument_validation_before_any_hip_call(lib):
     assert q(vp(0x10008), fake, fake, 1152, 1152, 1152, 10, 16, 72, 0, fake, fake, fake, fake, null) == 2
     assert q(fake, fake, fake, 1156, 1152, 1152, 10, 16, 72, 0, fake, fake, fake, fake, null) == 2
     assert q(fake, fake, fake, 15, 15, 15, 10, 3, 5, 0, fake, fake, fake, fake, null) == 2
+    # 32-bit chunk indices: T * H * d / 8 must stay below 2^31 (14913081 * 144 = 2^31 + 16)
+    assert q(fake, fake, fake, 1152, 1152, 1152, 14913081, 16, 72, 0, fake, fake, fake, fake, null) == 2
     a = lib.fp8vit_attn_varlen
     a.argtypes = [vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                   ctypes.c_float, vp, vp, ctypes.c_int64, vp]
@@ -70,6 +72,11 @@ def test_argument_validation_before_any_hip_call(lib):
     assert a(fake, fake, fake, fake, 1, 10, 10, 16, 72, 0.0, vp(0x10010), fake, 1152, null) == 2
     # empty problems are a no-op that never touches the device
     assert a(fake, fake, fake, fake, 0, 0, 0, 16, 72, 0.0, fake, fake, 1152, null) == 0
+    # size limits, first rejected size (the kernels address each e4m3 tensor with
+    # 31-bit offsets, up to three 128-key tiles past a segment's end): T = 1863752
+    # tokens of 16 x 72 gives (T + 384) * 1152 = 2^31 + 1024
+    assert a(fake, fake, fake, fake, 1, 1863752, 1863752, 16, 72, 0.0, fake, fake, 1152, null) == 2
+    assert a(fake, fake, fake, fake, 4, 1000, 1863752, 16, 72, 0.0, fake, fake, 1152, null) == 2
     f8 = lib.fp8vit_attn_varlen_fp8out
     f8.argtypes = [vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                    ctypes.c_float, vp, vp, vp, ctypes.c_int64, vp]
