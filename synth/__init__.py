@@ -35,6 +35,7 @@ __all__ = [
     "bf16_bits_to_f32",
     "make_qkv",
     "make_cu_seqlens",
+    "device_randn_bf16",
 ]
 
 
@@ -51,6 +52,22 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     """Exact widening of bf16 bit patterns to float32 (used to build inputs)."""
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def device_randn_bf16(shape: Sequence[int], seed: int, device, chunk: int = 1 << 28):
+    """Standard-normal bf16 tensor made on the device by torch's seeded
+    generator, a chunk of float32 samples at a time (rounded to nearest even).
+    For the sizes at the library's limits, which are too large to make on the
+    host; tests read back the slices they check."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    out = torch.empty(tuple(shape), dtype=torch.bfloat16, device=device)
+    flat = out.view(-1)
+    for i in range(0, flat.numel(), chunk):
+        n = min(chunk, flat.numel() - i)
+        flat[i:i + n] = torch.randn(n, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    return out
 
 
 def make_cu_seqlens(seglens: Sequence[int]) -> np.ndarray:
