@@ -13,10 +13,12 @@ from tests.gpu_helpers import codes_np, f32bits, fv, require_gpu, to_dev
 pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
 
 SEGLENS = (130, 0, 257, 64)
-H, D = 4, 72
+# (heads, head_dim): 4 heads run the narrow kernel; 64 heads the wide ones
+# (the 32x32-block kernel at head_dim 72, the wide 16x16 shape at 128)
+SHAPES = [(4, 72), (64, 72), (64, 128)]
 
 
-def _inputs(seed):
+def _inputs(seed, H, D):
     cu = make_cu_seqlens(SEGLENS)
     return make_qkv(seed, int(cu[-1]), H, D), cu
 
@@ -27,10 +29,11 @@ def _forward(bufs, st, mode, cu_d, maxlen):
     fv.attn_varlen(q8, k8, v8, cu_d, maxlen, st, out=out)
 
 
+@pytest.mark.parametrize("H,D", SHAPES)
 @pytest.mark.parametrize("mode", ["static", "dynamic"])
-def test_graph_replays_match_eager(mode):
+def test_graph_replays_match_eager(mode, H, D):
     dev = require_gpu()
-    (qb, kb, vb), cu = _inputs(1)
+    (qb, kb, vb), cu = _inputs(1, H, D)
     T = int(cu[-1])
     cu_d = torch.from_numpy(np.asarray(cu, np.int32)).to(dev)
     maxlen = max(SEGLENS)
@@ -59,7 +62,7 @@ def test_graph_replays_match_eager(mode):
     ring = oracle.scales.AmaxRing()
     n_replays = 40 if mode == "dynamic" else 6
     for r in range(n_replays):
-        (q2, k2, v2), _ = _inputs(100 + r)
+        (q2, k2, v2), _ = _inputs(100 + r, H, D)
         for buf, x in zip(bufs[:3], (q2, k2, v2)):
             buf.copy_(to_dev(x, dev))
         torch.cuda.synchronize()
