@@ -16,7 +16,8 @@ from tests.gpu_helpers import (ATOL_FRAC_OF_VMAX, REL_RMS_VS_FP64, codes_np, fv,
 pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
 
 
-def run_gpu(qb, kb, vb, cu, dev, mode="dynamic", static_values=None, softmax_scale=0.0, canary=True):
+def run_gpu(qb, kb, vb, cu, dev, mode="dynamic", static_values=None, softmax_scale=0.0, canary=True,
+            max_seqlen=None):
     st = fv.new_state(dev)
     if mode == "static":
         fv.state_set_static(st, static_values)
@@ -24,8 +25,10 @@ def run_gpu(qb, kb, vb, cu, dev, mode="dynamic", static_values=None, softmax_sca
     T, H, d = qb.shape
     out = torch.full((T, H, d), float("nan"), dtype=torch.bfloat16, device=dev) if canary else None
     seglens = np.diff(cu)
+    if max_seqlen is None:
+        max_seqlen = int(seglens.max()) if len(seglens) else 0
     out = fv.attn_varlen(q8, k8, v8, torch.from_numpy(np.asarray(cu, np.int32)).to(dev),
-                         int(seglens.max()) if len(seglens) else 0, st, softmax_scale, out=out)
+                         max_seqlen, st, softmax_scale, out=out)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), (q8, k8, v8), st
 
@@ -83,6 +86,9 @@ def test_attention_invariants(H, d):
     # run-to-run determinism (no float atomics in the accumulation)
     o2, _, _ = run_gpu(qb, kb, vb, cu, dev)
     assert np.array_equal(o, o2)
+    # max_seqlen is an upper bound: an overestimate only adds work items that exit
+    o3, _, _ = run_gpu(qb, kb, vb, cu, dev, max_seqlen=5000)
+    assert np.array_equal(o, o3)
     # one-token segment returns its own (dequantized) v, rounded to bf16
     dv = fv.state_read(st)["descale_used"][2]
     vhat = oracle.quant.dequantize(codes_np(codes[2])[130], dv)
