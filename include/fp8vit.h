@@ -146,8 +146,11 @@ fp8vit_status fp8vit_quantize_qkv(const void* q, const void* k, const void* v,
  *                 >= H*d, multiple of 4), 8-byte aligned. Every element of
  *                 every row of every segment is written.
  * O = softmax(Q^ K^T * scale) V^ per segment and head, where Q^ K^ V^ are the
- * dequantized e4m3 tensors; products on FP8 MFMA with fp32 accumulation; the
- * probabilities are carried to the P.V product in two e4m3 terms.
+ * dequantized e4m3 tensors. Q^ K^T runs on the FP8 MFMA with fp32
+ * accumulation; the probabilities reach the P.V product with more than e4m3
+ * precision: rounded once to f16 against V widened exactly to f16 (the
+ * kernels for grids that cover the chip), or as two e4m3 terms on the FP8
+ * MFMA (the smaller grids). fp32 accumulation throughout.
  * Errors: ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED (also when
  * (total_tokens + 384) * H * d reaches 2^31: the kernel addresses each e4m3
  * tensor with 31-bit offsets), ERR_HIP. */
