@@ -40,8 +40,13 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
-    p.add_argument("--warmup", type=int, default=100,
-                   help="untimed steps first; the GPU clock needs some tens of ms of load to settle")
+    p.add_argument("--warmup", type=int, default=100, help="untimed steps just before the timed block")
+    p.add_argument("--settle-s", type=float, default=2.0,
+                   help="untimed clock-settle phase before the warm-up: steps run back to back for this many "
+                        "seconds of wall time, whatever --warmup says (the shader clock ramps up under load)")
+    p.add_argument("--repeats", type=int, default=10,
+                   help="after the timed block, this many more blocks of --steps steps give the median and "
+                        "p10/p90 of the time per step")
     p.add_argument("--workload", default="l8192_hd72_static")
     p.add_argument("--rotate-mb", type=float, default=600.0,
                    help="cycle through input copies totalling at least this many MB (defeats the 256 MB MALL)")
@@ -213,6 +218,96 @@ def attn_traffic(workload, head_dim):
     return int(float(fields["traffic bytes per launch"]))
 
 
+class ClockSampler:
+    """Shader clock (MHz) of the benchmarked GPU from the SMU metrics table
+    (amdsmi, the library behind amd-smi). Best effort: on any failure the
+    readings are None and the reason is kept in `error`. `start()` begins
+    sampling from a background thread (every ~0.5 ms while the main thread
+    waits for the GPU), `stop()` returns the samples taken since."""
+
+    def __init__(self, dev_index):
+        import threading
+        self.h, self.error, self._amdsmi = None, None, None
+        self._lock, self._stop, self._thread, self._samples = threading.Lock(), threading.Event(), None, []
+        try:
+            import amdsmi
+            import torch
+            amdsmi.amdsmi_init()
+            self._amdsmi = amdsmi
+            props = torch.cuda.get_device_properties(dev_index)
+            want = (props.pci_domain_id, props.pci_bus_id, props.pci_device_id)
+            handles = amdsmi.amdsmi_get_processor_handles()
+            for h in handles:
+                dom, bus, rest = amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")
+                if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                    self.h = h
+            if self.h is None and len(handles) == 1:
+                self.h = handles[0]
+            if self.h is None:
+                self.error = "no amdsmi handle matches the PCI address of cuda:%d" % dev_index
+            else:
+                self.read()
+        except Exception as e:  # noqa: BLE001 - best effort only
+            self.h, self.error = None, "%s: %s" % (type(e).__name__, e)
+
+    def read(self):
+        """Current shader clock in MHz (mean over the XCDs that report one)."""
+        if self.h is None:
+            return None
+        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self.h)
+        clks = m.get("current_gfxclks")
+        if isinstance(clks, list):
+            vals = [c for c in clks if isinstance(c, (int, float)) and 0 < c < 10000]
+            if vals:
+                return float(sum(vals)) / len(vals)
+        for key in ("current_gfxclk", "average_gfxclk_frequency"):
+            c = m.get(key)
+            if isinstance(c, (int, float)) and 0 < c < 10000:
+                return float(c)
+        return None
+
+    def safe_read(self):
+        try:
+            return self.read()
+        except Exception as e:  # noqa: BLE001
+            self.error = "%s: %s" % (type(e).__name__, e)
+            return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            c = self.safe_read()
+            if c is not None:
+                with self._lock:
+                    self._samples.append(c)
+            self._stop.wait(0.0005)
+
+    def start(self):
+        import threading
+        if self.h is None:
+            return
+        self._samples, self._stop = [], threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        if self._thread is None:
+            return []
+        self._stop.set()
+        self._thread.join()
+        self._thread = None
+        with self._lock:
+            return list(self._samples)
+
+
+def _r(x, nd):
+    return None if x is None else round(float(x), nd)
+
+
+def _pct(xs, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q)) if xs else None
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -264,18 +359,32 @@ def main():
         fv.quantize_qkv(q, k, v, st, w.mode, out=(q8, k8, v8))
         attend()
 
+    clock = ClockSampler(dev.index or 0)
+    clock_idle = clock.safe_read()
+    # Clock settle: the shader clock ramps up over some tens of ms of load, so
+    # steps run back to back (in batches of 10, one wait per batch) for a fixed
+    # wall time before the warm-up, whatever --warmup is.
+    settle_steps, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < args.settle_s:
+        for _ in range(10):
+            step(settle_steps)
+            settle_steps += 1
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - t0
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     # Per-kernel durations: HIP events around the two launches of every
-    # `kernel_events_every`-th timed step. An event record costs a few us of
-    # device time here (three per step add ~11 us to a ~300 us step), so the
-    # other steps run without them.
+    # `kernel_events_every`-th timed step (from step every // 2 on). An event
+    # record costs a few us of device time here (three per step add ~11 us to a
+    # ~300 us step), so the other steps run without them.
     every = max(1, args.kernel_events_every)
-    sampled = [i for i in range(args.steps) if i % every == 0]
+    sampled = [i for i in range(args.steps) if i % every == every // 2] or [0]
     ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    clock_before = clock.safe_read()
+    clock.start()
     t_wall = time.perf_counter()
     start.record()
     for i in range(args.steps):
@@ -292,10 +401,40 @@ def main():
     end.record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
+    clock_during = clock.stop()
+    clock_after = clock.safe_read()
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / args.steps
-    quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev.values()]))
-    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev.values()]))
+    quant_samples = [e[0].elapsed_time(e[1]) for e in ev.values()]
+    attn_samples = [e[1].elapsed_time(e[2]) for e in ev.values()]
+
+    # Repeated blocks: `repeats` more blocks of the same steps, each bracketed
+    # by its own events, give the spread of the time per step; the middle step
+    # of each block also brackets its two launches (more per-kernel samples).
+    block_ms = []
+    for _ in range(max(0, args.repeats)):
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        mid = args.steps // 2
+        b0.record()
+        for i in range(args.steps):
+            q, k, v = sets[i % n_sets]
+            if i == mid:
+                e[0].record()
+            fv.quantize_qkv(q, k, v, st, w.mode, out=(q8, k8, v8))
+            if i == mid:
+                e[1].record()
+            attend()
+            if i == mid:
+                e[2].record()
+        b1.record()
+        torch.cuda.synchronize()
+        block_ms.append(b0.elapsed_time(b1) / args.steps)
+        quant_samples.append(e[0].elapsed_time(e[1]))
+        attn_samples.append(e[1].elapsed_time(e[2]))
+    clock_end = clock.safe_read()
+    quant_ms = float(np.mean(quant_samples))
+    attn_ms = float(np.mean(attn_samples))
 
     # Hot: the same steps on one input set, so that its 85 MB (at L = 8192) can stay
     # in the 256 MB MALL between steps; reported beside the rotated figure.
@@ -370,8 +509,21 @@ def main():
                    "scaling": w.mode + (" (1.5 x calibrated)" if w.mode == "static" else " (16-slot ring)"),
                    "outlier_frac": w.outlier_frac, "input_sets_rotated": n_sets},
         "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
+        "settle": {"seconds": round(settle_s, 3), "steps": settle_steps},
+        "blocks": {"n": len(block_ms), "steps_each": args.steps,
+                   "median_ms_per_step": _r(_pct(block_ms, 50), 4), "p10_ms_per_step": _r(_pct(block_ms, 10), 4),
+                   "p90_ms_per_step": _r(_pct(block_ms, 90), 4),
+                   "median_value": _r(w.flops / (_pct(block_ms, 50) * 1e-3) / 1e12, 2) if block_ms else None},
+        "clock_mhz": {"idle": clock_idle, "before": clock_before, "after": clock_after, "end": clock_end,
+                      "during_timed_block": {"n": len(clock_during), "min": _r(min(clock_during), 1),
+                                             "median": _r(_pct(clock_during, 50), 1),
+                                             "max": _r(max(clock_during), 1)} if clock_during else None,
+                      "source": "amdsmi gpu_metrics current_gfxclks (mean over XCDs)",
+                      **({"error": clock.error} if clock.error else {})},
         "kernels": {"quantize_ms": round(quant_ms, 4), "attention_ms": round(attn_ms, 4),
-                    "event_samples": len(sampled),
+                    "attention_ms_median": round(_pct(attn_samples, 50), 4),
+                    "quantize_ms_median": round(_pct(quant_samples, 50), 4),
+                    "event_samples": len(attn_samples),
                     "quantize_GBps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
                     "attention_TFLOPs": round(attn_tflops, 2)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": FP8_PEAK_TFLOPS,
