@@ -111,7 +111,8 @@ def state_bytes() -> int:
 
 
 def state_init(state: torch.Tensor) -> torch.Tensor:
-    _check("fp8vit_state_init", _lib.fp8vit_state_init(_ptr(state), _stream(state.device)))
+    state = _state_tensor(state)
+    _check("fp8vit_state_init", _lib.fp8vit_state_init(_ptr(state), _stream(_same_gpu(state=state))))
     return state
 
 
@@ -122,52 +123,134 @@ def new_state(device="cuda") -> torch.Tensor:
 
 
 def state_set_static(state: torch.Tensor, values_qkv: Sequence[float]) -> None:
+    state = _state_tensor(state)
     arr = (_f32 * 3)(*[float(x) for x in values_qkv])
-    _check("fp8vit_state_set_static", _lib.fp8vit_state_set_static(_ptr(state), arr, _stream(state.device)))
+    _check("fp8vit_state_set_static", _lib.fp8vit_state_set_static(_ptr(state), arr, _stream(_same_gpu(state=state))))
 
 
 def scales_update(state: torch.Tensor, amax_qkv: torch.Tensor) -> None:
     """Push a device float32[3] amax triple into the ring (bookkeeping only)."""
-    assert amax_qkv.dtype == torch.float32 and amax_qkv.numel() == 3 and amax_qkv.is_contiguous()
-    _check("fp8vit_scales_update", _lib.fp8vit_scales_update(_ptr(state), _ptr(amax_qkv), _stream(state.device)))
+    state = _state_tensor(state)
+    amax_qkv = _tensor("amax_qkv", amax_qkv)
+    if amax_qkv.dtype != torch.float32 or amax_qkv.numel() != 3 or not amax_qkv.is_contiguous():
+        raise ValueError("amax_qkv must be a contiguous float32 tensor of 3 elements")
+    dev = _same_gpu(state=state, amax_qkv=amax_qkv)
+    _check("fp8vit_scales_update", _lib.fp8vit_scales_update(_ptr(state), _ptr(amax_qkv), _stream(dev)))
+
+
+# Argument checks. They run before any library call, so a caller's mistake
+# raises ValueError here instead of reaching a kernel with a wrong pointer,
+# shape or stride. The library checks sizes and alignment again on its side.
+_CODE_DTYPES = (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))
+
+
+def _tensor(name: str, t) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    return t
+
+
+def _bhd(name: str, t, dtypes, shape=None, contiguous=False) -> torch.Tensor:
+    """A [T, H, d] tensor with heads and head_dim contiguous (token stride free
+    unless `contiguous`)."""
+    t = _tensor(name, t)
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must have dtype {' or '.join(str(x) for x in dtypes)}, got {t.dtype}")
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be 3-D [tokens, heads, head_dim], got shape {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    T, H, d = t.shape
+    if T > 0 and H > 0 and d > 0:
+        if (H > 1 and t.stride(1) != d) or (d > 1 and t.stride(2) != 1):
+            raise ValueError(f"{name}: heads and head_dim must be contiguous (strides {t.stride()})")
+        if contiguous and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [T, H, d]")
+        if t.stride(0) < H * d:
+            raise ValueError(f"{name}: token stride {t.stride(0)} is below H*d = {H * d}")
+    return t
+
+
+def _state_tensor(state) -> torch.Tensor:
+    state = _tensor("state", state)
+    if state.dtype != torch.uint8 or not state.is_contiguous() or state.numel() < state_bytes():
+        raise ValueError(f"state must be a contiguous uint8 tensor of at least {state_bytes()} bytes "
+                         "(use new_state())")
+    return state
+
+
+def _same_gpu(**tensors) -> torch.device:
+    """All tensors on one device, and that device a GPU."""
+    devs = {name: t.device for name, t in tensors.items() if t is not None}
+    first = next(iter(devs.values()))
+    if any(d != first for d in devs.values()):
+        raise ValueError("tensors are on different devices: " + ", ".join(f"{n}={d}" for n, d in devs.items()))
+    if first.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, got {first}")
+    return first
 
 
 def _token_stride(x: torch.Tensor) -> int:
     T, H, d = x.shape
-    if x.stride(2) != 1 or x.stride(1) != d:
-        raise ValueError("expected [T, H, d] with heads and head_dim contiguous")
     return x.stride(0) if T > 0 else H * d
+
+
+def _cu_seqlens(cu, T: int) -> torch.Tensor:
+    cu = _tensor("cu_seqlens", cu)
+    if cu.dtype != torch.int32 or cu.dim() != 1 or cu.numel() < 1 or not cu.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor of num_segments + 1 entries")
+    return cu
 
 
 def quantize_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state: torch.Tensor, mode="dynamic",
                  out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
     """bf16 [T, H, d] (token stride may exceed H*d) -> e4m3 codes as uint8 [T, H, d]."""
-    for x in (q, k, v):
-        if x.dtype != torch.bfloat16 or x.dim() != 3:
-            raise ValueError("q, k, v must be bf16 [T, H, d]")
+    q = _bhd("q", q, (torch.bfloat16,))
+    k = _bhd("k", k, (torch.bfloat16,), shape=q.shape)
+    v = _bhd("v", v, (torch.bfloat16,), shape=q.shape)
     T, H, d = q.shape
+    state = _state_tensor(state)
+    if mode not in _MODES and mode not in (FP8VIT_DYNAMIC, FP8VIT_STATIC):
+        raise ValueError(f"mode must be 'dynamic' or 'static', got {mode!r}")
+    if out is not None:
+        if not isinstance(out, (tuple, list)) or len(out) != 3:
+            raise ValueError("out must be a tuple of three [T, H, d] uint8 tensors")
+        out = tuple(_bhd(n, o, _CODE_DTYPES, shape=q.shape, contiguous=True) for n, o in zip(("q8", "k8", "v8"), out))
+    dev = _same_gpu(q=q, k=k, v=v, state=state, **({} if out is None else dict(zip(("q8", "k8", "v8"), out))))
     if out is None:
-        out = tuple(torch.empty((T, H, d), dtype=torch.uint8, device=q.device) for _ in range(3))
+        out = tuple(torch.empty((T, H, d), dtype=torch.uint8, device=dev) for _ in range(3))
     m = _MODES[mode] if isinstance(mode, str) else int(mode)
     st = _lib.fp8vit_quantize_qkv(_ptr(q), _ptr(k), _ptr(v), _token_stride(q), _token_stride(k), _token_stride(v),
                                   T, H, d, m, _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _ptr(state),
-                                  _stream(q.device))
+                                  _stream(dev))
     _check("fp8vit_quantize_qkv", st)
     return out
+
+
+def _attn_inputs(q8, k8, v8, cu_seqlens, max_seqlen, state):
+    q8 = _bhd("q8", q8, _CODE_DTYPES, contiguous=True)
+    k8 = _bhd("k8", k8, _CODE_DTYPES, shape=q8.shape, contiguous=True)
+    v8 = _bhd("v8", v8, _CODE_DTYPES, shape=q8.shape, contiguous=True)
+    cu_seqlens = _cu_seqlens(cu_seqlens, q8.shape[0])
+    if int(max_seqlen) < 0:
+        raise ValueError("max_seqlen must be >= 0")
+    return q8, k8, v8, cu_seqlens, _state_tensor(state)
 
 
 def attn_varlen(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
                 state: torch.Tensor, softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Non-causal FP8 attention per packed segment; returns bf16 [T, H, d]."""
+    q8, k8, v8, cu_seqlens, state = _attn_inputs(q8, k8, v8, cu_seqlens, max_seqlen, state)
     T, H, d = q8.shape
-    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous():
-        raise ValueError("cu_seqlens must be a contiguous int32 device tensor")
+    if out is not None:
+        out = _bhd("out", out, (torch.bfloat16,), shape=q8.shape)
+    dev = _same_gpu(q8=q8, k8=k8, v8=v8, cu_seqlens=cu_seqlens, state=state, out=out)
     if out is None:
-        out = torch.empty((T, H, d), dtype=torch.bfloat16, device=q8.device)
+        out = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
     ld_out = out.stride(0) if T > 0 else H * d
     st = _lib.fp8vit_attn_varlen(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(cu_seqlens), cu_seqlens.numel() - 1,
                                  int(max_seqlen), T, H, d, float(softmax_scale), _ptr(state), _ptr(out), ld_out,
-                                 _stream(q8.device))
+                                 _stream(dev))
     _check("fp8vit_attn_varlen", st)
     return out
 
@@ -176,24 +259,29 @@ def attn_varlen_fp8out(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, cu_
                        max_seqlen: int, state: torch.Tensor, out_descale: torch.Tensor, softmax_scale: float = 0.0,
                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """As attn_varlen, with e4m3 codes of O / out_descale (device float32[1]) as uint8 [T, H, d]."""
+    q8, k8, v8, cu_seqlens, state = _attn_inputs(q8, k8, v8, cu_seqlens, max_seqlen, state)
     T, H, d = q8.shape
-    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous():
-        raise ValueError("cu_seqlens must be a contiguous int32 device tensor")
+    out_descale = _tensor("out_descale", out_descale)
     if out_descale.dtype != torch.float32 or out_descale.numel() != 1:
-        raise ValueError("out_descale must be a float32 device tensor of one element")
+        raise ValueError("out_descale must be a float32 tensor of one element")
+    if out is not None:
+        out = _bhd("out", out, _CODE_DTYPES, shape=q8.shape)
+    dev = _same_gpu(q8=q8, k8=k8, v8=v8, cu_seqlens=cu_seqlens, state=state, out_descale=out_descale, out=out)
     if out is None:
-        out = torch.empty((T, H, d), dtype=torch.uint8, device=q8.device)
+        out = torch.empty((T, H, d), dtype=torch.uint8, device=dev)
     ld_out = out.stride(0) if T > 0 else H * d
     st = _lib.fp8vit_attn_varlen_fp8out(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(cu_seqlens), cu_seqlens.numel() - 1,
                                         int(max_seqlen), T, H, d, float(softmax_scale), _ptr(state),
-                                        _ptr(out_descale), _ptr(out), ld_out, _stream(q8.device))
+                                        _ptr(out_descale), _ptr(out), ld_out, _stream(dev))
     _check("fp8vit_attn_varlen_fp8out", st)
     return out
 
 
 def state_read(state: torch.Tensor) -> dict:
+    state = _state_tensor(state)
     view = _StateView()
-    _check("fp8vit_state_read", _lib.fp8vit_state_read(_ptr(state), ctypes.byref(view), _stream(state.device)))
+    _check("fp8vit_state_read", _lib.fp8vit_state_read(_ptr(state), ctypes.byref(view),
+                                                       _stream(_same_gpu(state=state))))
     return {
         "ring": [[view.ring[x][i] for i in range(16)] for x in range(3)],
         "count": int(view.count),
@@ -215,14 +303,17 @@ def state_write(state: torch.Tensor, snapshot: dict) -> None:
         view.amax_last[x] = float(snapshot["amax_last"][x])
     view.count = int(snapshot["count"])
     view.flags = int(snapshot.get("flags", 0))
-    _check("fp8vit_state_write", _lib.fp8vit_state_write(_ptr(state), ctypes.byref(view), _stream(state.device)))
+    state = _state_tensor(state)
+    _check("fp8vit_state_write", _lib.fp8vit_state_write(_ptr(state), ctypes.byref(view),
+                                                         _stream(_same_gpu(state=state))))
 
 
 def calibrated_values(state: torch.Tensor, margin: float = 1.5) -> Tuple[float, float, float]:
     """fp32(margin x ring window max) per tensor, as a calibration saves them."""
+    state = _state_tensor(state)
     arr = (_f32 * 3)()
     _check("fp8vit_calibrated_values",
-           _lib.fp8vit_calibrated_values(_ptr(state), float(margin), arr, _stream(state.device)))
+           _lib.fp8vit_calibrated_values(_ptr(state), float(margin), arr, _stream(_same_gpu(state=state))))
     return (arr[0], arr[1], arr[2])
 
 

@@ -23,7 +23,7 @@ ARCH = "gfx950"
 # Packed fp32 VALU ops are kept out of generated code on purpose.
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{CSRC}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-SOURCES = ["state.hip", "quant.hip", "attn.hip", "api.cpp", "json_scales.cpp"]
+SOURCES = ["state.hip", "quant.hip", "attn.hip", "api.cpp", "json_scales.cpp", "device.cpp"]
 
 
 def _compile(src: str) -> str:

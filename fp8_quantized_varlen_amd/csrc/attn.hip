@@ -1158,18 +1158,6 @@ void attn_w32_kernel(AttnArgs a) {
 int attn_block_m(int head_dim) { return head_dim == 72 ? Shape<72, false>::BM : Shape<128, false>::BM; }
 
 namespace {
-int g_cus[64];
-int device_cus() {
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  int& n = g_cus[dev & 63];
-  if (n == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) n = v;
-  }
-  return n;
-}
-
 // Upper bound on query tiles of BM rows per head: every segment adds at most
 // one partial tile.
 int64_t tiles_ub(int bm, int64_t total_tokens, int64_t nseg, int64_t max_seqlen) {

@@ -25,6 +25,9 @@ struct alignas(256) DevState {
 };
 static_assert(sizeof(DevState) == 512, "state layout");
 
+// Compute units of the current device (cached per device; 0 on error).
+int device_cus();
+
 constexpr float kFp8Max = 448.0f;
 constexpr float kDescaleFloor = 1e-10f;
 

@@ -227,21 +227,6 @@ __global__ __launch_bounds__(kQuantThreads) void amax_kernel(QuantArgs a) {
   }
 }
 
-namespace {
-int g_cus[64];
-
-int device_cus() {
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  int& n = g_cus[dev & 63];
-  if (n == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) n = v;
-  }
-  return n;
-}
-}  // namespace
-
 hipError_t launch_quantize(const QuantArgs& a, bool dynamic, hipStream_t s) {
   const int cus = device_cus();
   if (cus == 0) return hipErrorInvalidDevice;

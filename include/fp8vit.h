@@ -67,11 +67,20 @@ typedef struct fp8vit_state_view {
 } fp8vit_state_view;
 
 /* Bytes of device memory one layer's state needs. The caller allocates it
- * (256-byte aligned) and calls fp8vit_state_init before first use. */
+ * (256-byte aligned) and calls fp8vit_state_init before first use. The state
+ * holds the 16-slot amax ring and count, the static values, the descales in
+ * use and the amax pass's reduction scratch.
+ * Source: vLLM page "FP8 ViT Encoder Attention", Usage (a 16-entry circular
+ * buffer of observed Q/K/V amax drives each forward's scale) and Scale File
+ * Format (per-layer static q/k/v values). */
 size_t fp8vit_state_bytes(void);
 
 /* Reset a state: empty ring (zeros), count 0, static values 0, descales 0.
- * Asynchronous (a small fill kernel, safe inside graph capture). */
+ * Asynchronous (a small fill kernel, safe inside graph capture).
+ * Errors: ERR_INVALID_ARGUMENT (null), ERR_UNSUPPORTED (not 256-byte
+ * aligned), ERR_HIP.
+ * Source: vLLM page "FP8 ViT Encoder Attention", Usage (dynamic scaling with
+ * no scale file starts from an empty amax ring). */
 fp8vit_status fp8vit_state_init(void* d_state, void* stream);
 
 /* Host only. Read the static q/k/v values of `layer_name` from the JSON scale
@@ -84,14 +93,20 @@ fp8vit_status fp8vit_state_init(void* d_state, void* stream);
  * read the file), ERR_PARSE (not JSON, or the layer entry is not an object),
  * ERR_NOT_FOUND (no such layer, or one of q/k/v missing). Unknown keys are
  * ignored; for repeated keys the last occurrence wins. out_qkv is written only
- * on FP8VIT_OK. */
+ * on FP8VIT_OK.
+ * Source: vLLM page "FP8 ViT Encoder Attention", Scale File Format (layer ->
+ * {"q", "k", "v"}; q_scale/k_scale/v_scale aliases) and Calibrate-Once Reuse
+ * Workflow (the saved values already carry the margin). */
 fp8vit_status fp8vit_load_static_scales(const char* json_path, const char* layer_name,
                                         float out_qkv[3]);
 
 /* Store static q/k/v values (as read from the scale file) in the state.
  * Values must be finite and > 0 (else ERR_INVALID_ARGUMENT). Asynchronous:
  * the values travel as kernel arguments, so `values_qkv` may be freed on
- * return. The ring is not touched. */
+ * return. The ring is not touched. A later FP8VIT_STATIC quantize uses
+ * descale = max(fp32(value / 448), 1e-10).
+ * Source: vLLM page "FP8 ViT Encoder Attention", Calibrate-Once Reuse
+ * Workflow, step 2 (serve with static scales: no dynamic overhead). */
 fp8vit_status fp8vit_state_set_static(void* d_state, const float values_qkv[3], void* stream);
 
 /* Dynamic scale bookkeeping alone (the same device code the fused quantizer
@@ -100,7 +115,10 @@ fp8vit_status fp8vit_state_set_static(void* d_state, const float values_qkv[3], 
  * count, and set descale_used[i] = max(fp32(W_i / 448), 1e-10) where W_i is
  * the maximum over all 16 ring slots after the push (vLLM page, Usage: the
  * 16-entry circular buffer of amax values drives the scale update;
- * atrex-bench #025 for the division and the floor). One thread on `stream`. */
+ * atrex-bench #025 for the division and the floor). One thread on `stream`.
+ * Errors: ERR_INVALID_ARGUMENT (null), ERR_UNSUPPORTED (misaligned), ERR_HIP.
+ * Source: vLLM page "FP8 ViT Encoder Attention", Usage; atrex-bench operator
+ * #025 "per_token_group_quant_fp8", Reference Implementation. */
 fp8vit_status fp8vit_scales_update(void* d_state, const float* d_amax_qkv, void* stream);
 
 /* Quantize Q, K and V to e4m3: one kernel launch in static mode, two in
@@ -121,9 +139,17 @@ fp8vit_status fp8vit_scales_update(void* d_state, const float* d_amax_qkv, void*
  * kept (a negative value that rounds to zero gives 0x80) (atrex-bench #025,
  * Reference Implementation). descale_used[3] in the state is written with the
  * descales used. total_tokens == 0 is allowed (tensor pointers may then be
- * null; dynamic mode records amax 0). Errors: ERR_INVALID_ARGUMENT (null pointer, negative size, unknown
- * mode, ld < H*d), ERR_UNSUPPORTED (misalignment, H*d not a multiple of 8),
- * ERR_HIP. */
+ * null; dynamic mode records amax 0). Dynamic mode is two launches, not one:
+ * the pages ask only that Q, K and V be quantized right before the attention
+ * call, and a single cooperative launch with a grid-wide barrier measured
+ * slower on MI355X at every size.
+ * Errors: ERR_INVALID_ARGUMENT (null pointer, negative size, unknown mode,
+ * ld < H*d), ERR_UNSUPPORTED (misalignment, H*d not a multiple of 8, or
+ * total_tokens * H * d / 8 >= 2^31), ERR_HIP.
+ * Source: vLLM page "FP8 ViT Encoder Attention", introduction (Q/K/V are
+ * quantized to FP8 on the fly just before the attention call) and Usage
+ * (dynamic scaling); atrex-bench operator #025 "per_token_group_quant_fp8",
+ * Reference Implementation (scale, division, clamp, e4m3fn cast). */
 fp8vit_status fp8vit_quantize_qkv(const void* q, const void* k, const void* v,
                                   int64_t ld_q, int64_t ld_k, int64_t ld_v,
                                   int32_t total_tokens, int32_t num_heads, int32_t head_dim,
@@ -153,7 +179,10 @@ fp8vit_status fp8vit_quantize_qkv(const void* q, const void* k, const void* v,
  * MFMA (the smaller grids). fp32 accumulation throughout.
  * Errors: ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED (also when
  * (total_tokens + 384) * H * d reaches 2^31: the kernel addresses each e4m3
- * tensor with 31-bit offsets), ERR_HIP. */
+ * tensor with 31-bit offsets), ERR_HIP.
+ * Source: vLLM page "FP8 ViT Encoder Attention", Requirements (a varlen
+ * FP8 attention call with one scale per tensor) and the note on ROCm (packed
+ * variable-length image and video batches attended natively). */
 fp8vit_status fp8vit_attn_varlen(const void* q8, const void* k8, const void* v8,
                                  const int32_t* d_cu_seqlens, int32_t num_segments,
                                  int32_t max_seqlen, int32_t total_tokens, int32_t num_heads,
@@ -171,7 +200,10 @@ fp8vit_status fp8vit_attn_varlen(const void* q8, const void* k8, const void* v8,
  * Each element is the input quantization formula applied to the attention
  * output O as formed in fp32: e4m3 RNE of clamp(fp32(O / s), +-448). Other
  * arguments and errors as fp8vit_attn_varlen (ERR_INVALID_ARGUMENT also for a
- * null d_out_descale). */
+ * null d_out_descale).
+ * Source: vLLM issue 29920 "Add support for fused fp8 output to
+ * FlashAttention 3" (attention writing FP8 for the next FP8 GEMM); the
+ * formula is atrex-bench operator #025, Reference Implementation. */
 fp8vit_status fp8vit_attn_varlen_fp8out(const void* q8, const void* k8, const void* v8,
                                         const int32_t* d_cu_seqlens, int32_t num_segments,
                                         int32_t max_seqlen, int32_t total_tokens, int32_t num_heads,
@@ -180,7 +212,11 @@ fp8vit_status fp8vit_attn_varlen_fp8out(const void* q8, const void* k8, const vo
                                         void* stream);
 
 /* Synchronous read-back of a state for tests and calibration (copies on
- * `stream`, then waits for it). Not for the hot path. */
+ * `stream`, then waits for it). Not for the hot path.
+ * Errors: ERR_INVALID_ARGUMENT (null), ERR_UNSUPPORTED (misaligned), ERR_HIP.
+ * Source: vLLM page "FP8 ViT Encoder Attention", Calibrate-Once Reuse
+ * Workflow, step 1 (the scales learned by dynamic scaling are read out and
+ * dumped). */
 fp8vit_status fp8vit_state_read(const void* d_state, fp8vit_state_view* out, void* stream);
 
 /* Synchronous write of a whole state, the inverse of fp8vit_state_read: ring,
@@ -190,7 +226,9 @@ fp8vit_status fp8vit_state_read(const void* d_state, fp8vit_state_view* out, voi
  * resumed: the forwards that follow behave as they would have in the process
  * that read the state. Ring, static, descale and amax entries must be finite
  * and >= 0 (else ERR_INVALID_ARGUMENT). Copies on `stream` and waits for it,
- * so it is not for graph capture. */
+ * so it is not for graph capture.
+ * Source: vLLM page "FP8 ViT Encoder Attention", Usage (the ring carries over
+ * from forward to forward, so resuming it needs its whole contents). */
 fp8vit_status fp8vit_state_write(void* d_state, const fp8vit_state_view* in, void* stream);
 
 /* Synchronous. The values a calibration saves (vLLM page "FP8 ViT Encoder
@@ -201,7 +239,9 @@ fp8vit_status fp8vit_state_write(void* d_state, const fp8vit_state_view* in, voi
  * pointer, margin not finite or <= 0, a product that overflows),
  * ERR_NOT_FOUND (a tensor whose ring holds no amax > 0: no dynamic forward has
  * been recorded, or every input was zero), ERR_HIP. out_qkv is written only on
- * FP8VIT_OK. */
+ * FP8VIT_OK.
+ * Source: vLLM page "FP8 ViT Encoder Attention", Calibrate-Once Reuse
+ * Workflow (16 dynamic passes, learned scales times the save margin). */
 fp8vit_status fp8vit_calibrated_values(const void* d_state, float margin, float out_qkv[3], void* stream);
 
 /* Host only. Store one layer's static q/k/v values in the JSON scale file at
@@ -216,11 +256,16 @@ fp8vit_status fp8vit_calibrated_values(const void* d_state, float margin, float 
  * as the shortest decimal that reads back to the same float. Errors:
  * ERR_INVALID_ARGUMENT (null argument; a value that is not finite and > 0),
  * ERR_PARSE (the existing file is not a JSON object: it is left untouched),
- * ERR_IO (cannot read the existing file, or cannot write or rename). */
+ * ERR_IO (cannot read the existing file, or cannot write or rename).
+ * Source: vLLM page "FP8 ViT Encoder Attention", Scale File Format and
+ * Calibrate-Once Reuse Workflow, step 1 (dump the learned scales to JSON). */
 fp8vit_status fp8vit_save_static_scales(const char* json_path, const char* layer_name,
                                         const float values_qkv[3]);
 
-/* Static string naming a status code. */
+/* Static string naming a status code; never NULL (unknown codes give
+ * "unknown status").
+ * Source: the failure cases of the calls above; the file errors (IO, PARSE,
+ * NOT_FOUND) are those of reading the vLLM page's Scale File Format. */
 const char* fp8vit_status_str(fp8vit_status status);
 
 #ifdef __cplusplus

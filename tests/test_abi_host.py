@@ -34,6 +34,32 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+PAGES = ('vLLM page "FP8 ViT Encoder Attention"', 'atrex-bench operator #025', 'vLLM issue 29920',
+         "FlashInfer PR", "Scale File Format")
+
+
+def header_declarations():
+    """(function name, the comment block right above its declaration)."""
+    txt = open(HEADER).read()
+    out = []
+    for m in re.finditer(r"/\*((?:(?!\*/).)*)\*/\s*\n([^;{]*?\b(fp8vit_[a-z0-9_]+)\s*\([^;]*\);)", txt, re.S):
+        out.append((m.group(3), m.group(1)))
+    return out
+
+
+def test_every_declaration_cites_its_passage():
+    """Each entry point's comment names the page and section that defines the
+    operation (a "Source:" line), or, for an entry point that the pages do not
+    define, the callers it is for."""
+    decls = header_declarations()
+    assert sorted(n for n, _ in decls) == header_functions()
+    for name, comment in decls:
+        flat = " ".join(comment.replace("*", " ").split())
+        m = re.search(r"Source: (.*)", flat)
+        assert m, f"{name}: no Source: line"
+        assert any(p in m.group(1) for p in PAGES) or "cannot allocate" in m.group(1), f"{name}: {m.group(1)}"
+
+
 def test_binding_declares_the_same_symbols():
     import fp8_quantized_varlen_amd as fv
     assert sorted(fv.EXPORTED_SYMBOLS) == header_functions()
