@@ -70,6 +70,7 @@ fp8vit_status fp8vit_quantize_qkv(const void* q, const void* k, const void* v, i
   a.y[2] = static_cast<uint8_t*>(v8);
   a.T = total_tokens;
   a.row8 = (int32_t)(row / 8);
+  a.amax_blocks = 0;
   a.st = static_cast<DevState*>(d_state);
   return from_hip(fp8vit::launch_quantize(a, mode == FP8VIT_DYNAMIC, as_stream(stream)));
 }
@@ -142,12 +143,18 @@ fp8vit_status fp8vit_state_read(const void* d_state, fp8vit_state_view* out, voi
   if (!d_state || !out) return FP8VIT_ERR_INVALID_ARGUMENT;
   if (!aligned(d_state, 256)) return FP8VIT_ERR_UNSUPPORTED;
   DevState h;
-  hipError_t e = hipMemcpyAsync(&h, d_state, sizeof(DevState), hipMemcpyDeviceToHost, as_stream(stream));
+  hipError_t e = hipMemcpyAsync(&h, d_state, fp8vit::kStateViewBytes, hipMemcpyDeviceToHost, as_stream(stream));
   if (e != hipSuccess) return FP8VIT_ERR_HIP;
   e = hipStreamSynchronize(as_stream(stream));
   if (e != hipSuccess) return FP8VIT_ERR_HIP;
   std::memcpy(out->ring, h.ring, sizeof(out->ring));
   out->count = h.count;
+  // The last dynamic forward's amax may still be pending: report the ring as
+  // it is once pushed (what the next amax pass does first on the device).
+  if (h.pending != 0u) {
+    for (int x = 0; x < 3; ++x) out->ring[x][h.count % FP8VIT_RING_SLOTS] = h.pending_amax[x];
+    out->count = h.count + 1;
+  }
   for (int i = 0; i < 3; ++i) {
     out->static_values[i] = h.static_values[i];
     out->descale_used[i] = h.descale_used[i];
@@ -167,8 +174,9 @@ fp8vit_status fp8vit_state_write(void* d_state, const fp8vit_state_view* in, voi
     if (!nonneg(in->static_values[x]) || !nonneg(in->descale_used[x]) || !nonneg(in->amax_last[x]))
       return FP8VIT_ERR_INVALID_ARGUMENT;
   }
-  // The atomic-max scratch and the arrival counter start from zero, as
-  // after fp8vit_state_init.
+  // No push is pending, and the partial maxima start from zero, as after
+  // fp8vit_state_init.
+  static_assert(sizeof(DevState) <= 32768, "state copied through the stack");
   DevState h;
   std::memset(&h, 0, sizeof(h));
   std::memcpy(h.ring, in->ring, sizeof(h.ring));

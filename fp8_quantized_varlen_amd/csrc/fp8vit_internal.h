@@ -3,27 +3,42 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "fp8vit.h"
 
 namespace fp8vit {
 
+// Blocks of the amax pass: at most this many per-block partial maxima fit in
+// the state.
+constexpr int kAmaxSlots = 1024;
+
 // Per-layer device state. The caller allocates fp8vit_state_bytes() bytes.
+// The first 512 bytes hold what fp8vit_state_read reports (plus the pending
+// ring push); the rest is the amax pass's per-block partial maxima.
+//
+// Dynamic bookkeeping is split over the two launches of a forward: the
+// quantize pass of forward n derives its descales from the ring and this
+// forward's amax and records that amax as pending (it cannot push it itself:
+// its other workgroups are still reading the ring); the amax pass of forward
+// n+1 (or fp8vit_scales_update) first pushes the pending amax into the ring.
+// fp8vit_state_read applies a pending push to the view it returns.
 struct alignas(256) DevState {
   float ring[3][FP8VIT_RING_SLOTS];  // observed amax of q, k, v
-  uint32_t count;                    // dynamic forwards recorded so far
+  uint32_t count;                    // dynamic forwards pushed into the ring
   float static_values[3];            // static q/k/v values (margin included)
   float descale_used[3];             // descales of the last quantize / update
   float amax_last[3];                // amax of the last dynamic forward
   uint32_t flags;                    // reserved: 0
-  uint32_t reserved0;
-  uint32_t amax_bits[2][4];          // atomic-max scratch of the amax pass (row 0); 0 between forwards
-  uint32_t bar_arrived;              // blocks of the amax pass that finished; 0 between forwards
-  uint32_t reserved2;
-  uint32_t reserved1[54];
+  uint32_t pending;                  // 1: pending_amax still has to be pushed
+  float pending_amax[3];
+  uint32_t reserved0[65];
+  uint32_t amax_part[kAmaxSlots][4];  // amax pass block b: |q|, |k|, |v| maxima (bf16 magnitude bits)
 };
-static_assert(sizeof(DevState) == 512, "state layout");
+constexpr size_t kStateViewBytes = 512;   // the reported part, before the partial maxima
+static_assert(offsetof(DevState, amax_part) == kStateViewBytes, "state layout");
+static_assert(sizeof(DevState) == 512 + 16 * kAmaxSlots, "state layout");
 
 // Compute units of the current device (cached per device; 0 on error).
 int device_cus();
@@ -42,6 +57,7 @@ struct QuantArgs {
   uint8_t* y[3];
   int32_t T;
   int32_t row8;   // H*d/8 (16-byte chunks per token row)
+  int32_t amax_blocks;  // workgroups of the amax pass (partial maxima to reduce)
   DevState* st;
 };
 hipError_t launch_quantize(const QuantArgs& a, bool dynamic, hipStream_t s);

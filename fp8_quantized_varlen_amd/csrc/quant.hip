@@ -18,8 +18,10 @@
 // Dynamic mode (vLLM page "FP8 ViT Encoder Attention", Usage): the amax of
 // each whole tensor is reduced first, pushed into the 16-slot ring, and the
 // window maximum sets this forward's descale. Two launches: the amax pass
-// (whose last block to finish does the ring bookkeeping) and the quantize
-// pass, which reads the descales from the state. A single cooperative launch
+// (per-block partial maxima in the state) and the quantize pass, whose every
+// block reduces those partials and takes its descales from the ring and this
+// forward's amax; the push of that amax into the ring is left pending in the
+// state and done by the next forward's amax pass (see DevState). A single cooperative launch
 // with a grid-wide barrier between the passes reads the input once, but on
 // MI355X it measured slower at every size: the cooperative launch itself adds
 // ~17 us and a barrier across eight XCDs costs several device-scope atomic
@@ -34,14 +36,21 @@
 namespace fp8vit {
 
 // Quantize pass: one 16-byte chunk of each of Q, K and V per thread and
-// iteration, up to 16 workgroups per CU (a small grid with several chunks in
-// flight per thread measured 9-14 % slower).
+// iteration. Static mode: up to 16 workgroups per CU, each chunk loaded,
+// converted and stored in turn (a small grid with several chunks in flight
+// per thread measured 9-14 % slower). Dynamic mode, whose prologue reduces
+// the amax pass's partial maxima before the descales are known: up to 4
+// workgroups per CU (one resident round), the first loads issued before the
+// prologue and each next chunk loaded before the current one is stored.
 constexpr int kQuantThreads = 512;
-constexpr int kUnroll = 1;
 constexpr int kGridPerCu = 16;
+constexpr int kGridPerCuDynamic = 4;
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
-constexpr int kAmaxBlocks = 128;
+// Amax pass: one workgroup per CU (at most kAmaxSlots), each thread with
+// kAmaxUnroll 16-byte chunks of each tensor in flight. Measured at L = 8192,
+// 16 heads: 1, 2 or 4 workgroups per CU and 2, 4 or 8 chunks within 5 %.
+constexpr int kAmaxBlocksPerCu = 1;
 constexpr int kAmaxUnroll = 4;
 __device__ __forceinline__ uint32_t bf16_lo(uint32_t w) { return w << 16; }
 __device__ __forceinline__ uint32_t bf16_hi(uint32_t w) { return w & 0xffff0000u; }
@@ -85,8 +94,6 @@ __device__ __forceinline__ const uint4* chunk_src(const uint16_t* x, int64_t ld,
   return reinterpret_cast<const uint4*>(x + (int64_t)t * ld + 8 * (int64_t)j);
 }
 
-// Quantize Q, K and V together: each thread keeps kUnroll chunks of each of
-// the three tensors in flight before converting and storing them.
 // NT: non-temporal loads and stores. They speed up the quantize pass of
 // dynamic mode (which re-reads what the amax pass has just read) by ~10 % and
 // slow the static pass slightly.
@@ -104,24 +111,32 @@ __device__ __forceinline__ void st8(uint2* p, uint2 v) {
   else *p = v;
 }
 template <bool CONTIG, bool NT>
+__device__ __forceinline__ void load3(const QuantArgs& a, uint32_t c, uint32_t n8, uint4 w[3]) {
+#pragma unroll
+  for (int x = 0; x < 3; ++x)
+    w[x] = c < n8 ? ld16<NT>(chunk_src<CONTIG>(a.x[x], a.ld[x], a.row8, c)) : make_uint4(0, 0, 0, 0);
+}
+
+// Quantize this thread's chunks c = gtid + i * gstride of Q, K and V.
+// PRELOADED: `w` already holds chunk gtid of each tensor (loaded before the
+// descales were known, so that the load latency overlaps the kernel's
+// prologue), and the next chunk's loads are issued before the current one is
+// converted and stored. Otherwise each chunk is loaded, converted and stored
+// in turn (`w` is scratch).
+template <bool CONTIG, bool NT, bool PRELOADED>
 __device__ __forceinline__ void quantize_all(const QuantArgs& a, uint32_t n8, const double* r, uint32_t gtid,
-                                             uint32_t gstride) {
-  for (uint32_t base = gtid; base < n8; base += gstride * kUnroll) {
-    uint4 w[3][kUnroll];
+                                             uint32_t gstride, uint4 w[3]) {
+  for (uint32_t c = gtid; c < n8; c += gstride) {
+    uint4 cur[3];
+    if (PRELOADED) {
 #pragma unroll
-    for (int x = 0; x < 3; ++x)
+      for (int x = 0; x < 3; ++x) cur[x] = w[x];
+      load3<CONTIG, NT>(a, c + gstride, n8, w);
+    } else {
+      load3<CONTIG, NT>(a, c, n8, cur);
+    }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const uint32_t c = base + u * gstride;
-        w[x][u] = c < n8 ? ld16<NT>(chunk_src<CONTIG>(a.x[x], a.ld[x], a.row8, c)) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-    for (int x = 0; x < 3; ++x)
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const uint32_t c = base + u * gstride;
-        if (c < n8) st8<NT>(reinterpret_cast<uint2*>(a.y[x]) + c, quant_chunk(w[x][u], r[x]));
-      }
+    for (int x = 0; x < 3; ++x) st8<NT>(reinterpret_cast<uint2*>(a.y[x]) + c, quant_chunk(cur[x], r[x]));
   }
 }
 
@@ -147,84 +162,92 @@ __device__ __forceinline__ void absmax_all(const QuantArgs& a, uint32_t n8, uint
   }
 }
 
-template <int THREADS>
-__device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* red) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+// Largest value of m[0..2] over the workgroup, in every thread (red: LDS
+// scratch of one triple per wave).
+__device__ __forceinline__ void block_max3(uint32_t m[3], uint32_t (*red)[3]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  uint32_t r = red[0];
 #pragma unroll
-  for (int i = 1; i < THREADS / 64; ++i) r = max(r, red[i]);
+  for (int x = 0; x < 3; ++x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m[x] = max(m[x], (uint32_t)__shfl_xor((int)m[x], off, 64));
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int x = 0; x < 3; ++x) red[wave][x] = m[x];
+  }
   __syncthreads();
-  return r;
+#pragma unroll
+  for (int x = 0; x < 3; ++x) {
+    m[x] = red[0][x];
+#pragma unroll
+    for (int w = 1; w < kQuantThreads / 64; ++w) m[x] = max(m[x], red[w][x]);
+  }
 }
 
 // Quantize pass. Static mode: the descales come from the stored static
-// values (block 0 records them). Dynamic mode: the amax pass already wrote
-// them to the state.
+// values (block 0 records them). Dynamic mode: every block reduces the amax
+// pass's per-block maxima to this forward's amax and takes the descales from
+// the window maximum over the ring slots other than count % 16 and that amax
+// (the ring itself is not changed here: block 0 records the amax as pending,
+// to be pushed by the next forward's amax pass).
 template <bool CONTIG, bool DYNAMIC>
 __global__ __launch_bounds__(kQuantThreads) void quant_kernel(QuantArgs a) {
   __shared__ double rcp[3];
-  const uint32_t gtid = blockIdx.x * kQuantThreads + threadIdx.x;
-  const uint32_t gstride = gridDim.x * kQuantThreads;
-  const uint32_t n8 = (uint32_t)a.T * (uint32_t)a.row8;
-  if (threadIdx.x == 0) {
-#pragma unroll
-    for (int x = 0; x < 3; ++x) {
-      const float d = DYNAMIC ? a.st->descale_used[x] : descale_from_amax(a.st->static_values[x]);
-      rcp[x] = 1.0 / (double)d;
-      if (!DYNAMIC && blockIdx.x == 0) a.st->descale_used[x] = d;
-    }
-  }
-  __syncthreads();
-  const double r[3] = {rcp[0], rcp[1], rcp[2]};
-  quantize_all<CONTIG, DYNAMIC>(a, n8, r, gtid, gstride);
-}
-
-// Amax pass of dynamic mode. Each block reduces its chunks of Q, K and V and
-// atomic-maxes the three results into the state's scratch; then it arrives at
-// a counter. The block that arrives last sees every other block's maxima
-// (each arrival is a release, the last one an acquire), pushes the triple
-// into ring slot count % 16, writes the descales from the window maximum
-// including it, and clears the scratch and the counter for the next forward.
-template <bool CONTIG>
-__global__ __launch_bounds__(kQuantThreads) void amax_kernel(QuantArgs a) {
-  __shared__ uint32_t red[kQuantThreads / 64];
-  __shared__ uint32_t is_last;
+  __shared__ uint32_t red[kQuantThreads / 64][3];
   const uint32_t gtid = blockIdx.x * kQuantThreads + threadIdx.x;
   const uint32_t gstride = gridDim.x * kQuantThreads;
   const uint32_t n8 = (uint32_t)a.T * (uint32_t)a.row8;
   DevState* st = a.st;
-  uint32_t mt[3];
-  absmax_all<CONTIG>(a, n8, gtid, gstride, mt);
+  uint4 w[3];
+  if (DYNAMIC) load3<CONTIG, true>(a, gtid, n8, w);   // in flight during the prologue
+  if (DYNAMIC) {
+    uint32_t m[3] = {0u, 0u, 0u};
+    for (int b = threadIdx.x; b < a.amax_blocks; b += kQuantThreads) {
+      const uint4 part = *reinterpret_cast<const uint4*>(st->amax_part[b]);
+      m[0] = max(m[0], part.x);
+      m[1] = max(m[1], part.y);
+      m[2] = max(m[2], part.z);
+    }
+    block_max3(m, red);
+    if (threadIdx.x == 0) {
+      float amax[3], d[3];
 #pragma unroll
-  for (int x = 0; x < 3; ++x) {
-    const uint32_t m = block_max<kQuantThreads>(mt[x], red);
-    if (threadIdx.x == 0 && m != 0u)
-      __hip_atomic_fetch_max(&st->amax_bits[0][x], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  if (threadIdx.x == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(&st->bar_arrived, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = prev + 1 == gridDim.x;
-  }
-  __syncthreads();
-  if (is_last && threadIdx.x == 0) {
-    float amax[3], d[3];
+      for (int x = 0; x < 3; ++x) amax[x] = __uint_as_float(m[x] << 16);
+      ring_window_descales(st, st->count, amax, d);
+#pragma unroll
+      for (int x = 0; x < 3; ++x) rcp[x] = 1.0 / (double)d[x];
+      if (blockIdx.x == 0) record_pending(st, amax, d);
+    }
+  } else if (threadIdx.x == 0) {
 #pragma unroll
     for (int x = 0; x < 3; ++x) {
-      const uint32_t bits = __hip_atomic_load(&st->amax_bits[0][x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      amax[x] = __uint_as_float(bits << 16);
+      const float d = descale_from_amax(st->static_values[x]);
+      rcp[x] = 1.0 / (double)d;
+      if (blockIdx.x == 0) st->descale_used[x] = d;
     }
-    const uint32_t count = st->count;
-    ring_window_descales(st, count, amax, d);
-    ring_commit(st, count, amax, d);
-#pragma unroll
-    for (int x = 0; x < 3; ++x)
-      __hip_atomic_store(&st->amax_bits[0][x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&st->bar_arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  __syncthreads();
+  const double r[3] = {rcp[0], rcp[1], rcp[2]};
+  quantize_all<CONTIG, DYNAMIC, DYNAMIC>(a, n8, r, gtid, gstride, w);
+}
+
+// Amax pass of dynamic mode. Each block reduces its chunks of Q, K and V and
+// stores the three maxima in its own slot of the state; there are no
+// atomics and no last-block step (the quantize pass reduces the slots).
+// Block 0 first pushes the amax the previous dynamic forward left pending:
+// nothing else reads the ring during this pass.
+template <bool CONTIG>
+__global__ __launch_bounds__(kQuantThreads) void amax_kernel(QuantArgs a) {
+  __shared__ uint32_t red[kQuantThreads / 64][3];
+  const uint32_t gtid = blockIdx.x * kQuantThreads + threadIdx.x;
+  const uint32_t gstride = gridDim.x * kQuantThreads;
+  const uint32_t n8 = (uint32_t)a.T * (uint32_t)a.row8;
+  DevState* st = a.st;
+  if (blockIdx.x == 0 && threadIdx.x == 0) ring_push_pending(st);
+  uint32_t m[3];
+  absmax_all<CONTIG>(a, n8, gtid, gstride, m);
+  block_max3(m, red);
+  if (threadIdx.x == 0) *reinterpret_cast<uint4*>(st->amax_part[blockIdx.x]) = make_uint4(m[0], m[1], m[2], 0u);
 }
 
 hipError_t launch_quantize(const QuantArgs& a, bool dynamic, hipStream_t s) {
@@ -232,22 +255,29 @@ hipError_t launch_quantize(const QuantArgs& a, bool dynamic, hipStream_t s) {
   if (cus == 0) return hipErrorInvalidDevice;
   const bool contig = a.ld[0] == 8LL * a.row8 && a.ld[1] == 8LL * a.row8 && a.ld[2] == 8LL * a.row8;
   const uint64_t n8 = (uint64_t)a.T * (uint64_t)a.row8;
-  uint64_t g = (n8 + (uint64_t)kQuantThreads * kUnroll - 1) / ((uint64_t)kQuantThreads * kUnroll);
+  uint64_t g = (n8 + (uint64_t)kQuantThreads - 1) / (uint64_t)kQuantThreads;
   if (g < 1) g = 1;
-  if (g > (uint64_t)cus * kGridPerCu) g = (uint64_t)cus * kGridPerCu;
+  const uint64_t gmax = (uint64_t)cus * (dynamic ? kGridPerCuDynamic : kGridPerCu);
+  if (g > gmax) g = gmax;
   const dim3 grid((unsigned)g), block(kQuantThreads);
   if (dynamic) {
-    const dim3 agrid((unsigned)(g < (uint64_t)kAmaxBlocks ? g : (uint64_t)kAmaxBlocks));
+    uint64_t ga = (n8 + (uint64_t)kQuantThreads * kAmaxUnroll - 1) / ((uint64_t)kQuantThreads * kAmaxUnroll);
+    if (ga < 1) ga = 1;
+    if (ga > (uint64_t)cus * kAmaxBlocksPerCu) ga = (uint64_t)cus * kAmaxBlocksPerCu;
+    if (ga > (uint64_t)kAmaxSlots) ga = kAmaxSlots;
+    const dim3 agrid((unsigned)ga);
+    QuantArgs ad = a;
+    ad.amax_blocks = (int32_t)ga;
     if (contig)
-      hipLaunchKernelGGL(amax_kernel<true>, agrid, block, 0, s, a);
+      hipLaunchKernelGGL(amax_kernel<true>, agrid, block, 0, s, ad);
     else
-      hipLaunchKernelGGL(amax_kernel<false>, agrid, block, 0, s, a);
+      hipLaunchKernelGGL(amax_kernel<false>, agrid, block, 0, s, ad);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (contig)
-      hipLaunchKernelGGL((quant_kernel<true, true>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((quant_kernel<true, true>), grid, block, 0, s, ad);
     else
-      hipLaunchKernelGGL((quant_kernel<false, true>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((quant_kernel<false, true>), grid, block, 0, s, ad);
   } else {
     if (contig)
       hipLaunchKernelGGL((quant_kernel<true, false>), grid, block, 0, s, a);

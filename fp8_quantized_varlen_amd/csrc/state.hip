@@ -28,16 +28,19 @@ __global__ void scales_update_kernel(DevState* st, const float* amax) {
   if (threadIdx.x == 0) {
     float a[3] = {amax[0], amax[1], amax[2]};
     float d[3];
+    ring_push_pending(st);
     ring_window_descales(st, st->count, a, d);
-    ring_commit(st, st->count, a, d);
-    // The amax pass leaves its scratch at zero; keep it so.
-    for (int p = 0; p < 2; ++p)
-      for (int x = 0; x < 4; ++x) st->amax_bits[p][x] = 0u;
+    ring_push(st, a);
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+      st->amax_last[x] = a[x];
+      st->descale_used[x] = d[x];
+    }
   }
 }
 
 hipError_t launch_state_init(DevState* st, hipStream_t s) {
-  hipLaunchKernelGGL(state_init_kernel, dim3(1), dim3(128), 0, s, st);
+  hipLaunchKernelGGL(state_init_kernel, dim3(1), dim3(256), 0, s, st);
   return hipGetLastError();
 }
 
