@@ -3,7 +3,9 @@
 
 One step = the whole hot path on one batch already resident in HBM:
 fp8vit_quantize_qkv (amax + scale bookkeeping in dynamic mode, e4m3
-quantization of Q, K and V) followed by fp8vit_attn_varlen. Throughput counts
+quantization of Q, K and V) followed by fp8vit_attn_varlen_ws (the attention
+with a workspace, which splits the keys of grids too small to fill the GPU;
+the same kernel and result as fp8vit_attn_varlen otherwise). Throughput counts
 the useful attention flops 4*H*d*sum(L_i^2) per step.
 
 Default workload: one 8192-token segment, 16 heads, head_dim 72, static scales
@@ -347,11 +349,15 @@ def main():
     out8 = torch.empty((T, H, d), dtype=torch.uint8, device=dev) if args.out == "fp8" else None
     out_descale = torch.tensor([0.0025], dtype=torch.float32, device=dev)
 
+    # workspace for the key split of grids too small to fill the GPU (0 bytes when it would not split)
+    ws_bytes = fv.attn_workspace_bytes(len(w.seglens), max_seqlen, T, H, d)
+    ws = fv.attn_workspace(len(w.seglens), max_seqlen, T, H, d, device=dev)
+
     def attend():
         if out8 is not None:
             fv.attn_varlen_fp8out(q8, k8, v8, cu, max_seqlen, st, out_descale, out=out8)
         else:
-            fv.attn_varlen(q8, k8, v8, cu, max_seqlen, st, out=out)
+            fv.attn_varlen_ws(q8, k8, v8, cu, max_seqlen, st, ws, out=out)
     torch.cuda.synchronize()
 
     def step(i):
@@ -506,6 +512,7 @@ def main():
         "dtype": "fp8e4m3+f16" if kname.startswith("attn_w32") or kname.endswith(", true>") else "fp8e4m3",
         "data": "synthetic",
         "config": {"workload": w.name, "segments": list(w.seglens), "heads": H, "head_dim": d, "output": args.out,
+                   "key_split_workspace_bytes": ws_bytes if out8 is None else 0,
                    "scaling": w.mode + (" (1.5 x calibrated)" if w.mode == "static" else " (16-slot ring)"),
                    "outlier_frac": w.outlier_frac, "input_sets_rotated": n_sets},
         "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),

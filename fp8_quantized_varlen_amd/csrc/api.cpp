@@ -80,7 +80,10 @@ namespace {
 fp8vit_status attn_common(const void* q8, const void* k8, const void* v8, const int32_t* d_cu_seqlens,
                           int32_t num_segments, int32_t max_seqlen, int32_t total_tokens, int32_t num_heads,
                           int32_t head_dim, float softmax_scale, const void* d_state, void* out, bool out_fp8,
-                          const float* d_out_descale, int64_t ld_out, void* stream) {
+                          const float* d_out_descale, int64_t ld_out, void* d_workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (workspace_bytes > 0 && (!d_workspace || !aligned(d_workspace, 256)))
+    return d_workspace ? FP8VIT_ERR_UNSUPPORTED : FP8VIT_ERR_INVALID_ARGUMENT;
   if (!d_cu_seqlens || !d_state) return FP8VIT_ERR_INVALID_ARGUMENT;
   if (out_fp8 && !d_out_descale) return FP8VIT_ERR_INVALID_ARGUMENT;
   if (num_segments < 0 || max_seqlen < 0 || total_tokens < 0 || num_heads <= 0) return FP8VIT_ERR_INVALID_ARGUMENT;
@@ -118,6 +121,17 @@ fp8vit_status attn_common(const void* q8, const void* k8, const void* v8, const 
   a.out_descale = d_out_descale;
   a.ld_out = ld_out;
   a.softmax_scale = softmax_scale > 0.0f ? softmax_scale : (float)(1.0 / std::sqrt((double)head_dim));
+  a.nsplit = 1;
+  a.ws_slots = nullptr;
+  if (workspace_bytes > 0) {
+    size_t need = 0;
+    const int sp = fp8vit::attn_split_plan(head_dim, num_heads, total_tokens, num_segments, max_seqlen,
+                                           workspace_bytes, &need);
+    if (sp > 1) {
+      a.nsplit = sp;
+      a.ws_slots = static_cast<uint8_t*>(d_workspace);
+    }
+  }
   return from_hip(fp8vit::launch_attn(a, head_dim, total_tokens, max_seqlen, as_stream(stream)));
 }
 }  // namespace
@@ -127,7 +141,24 @@ fp8vit_status fp8vit_attn_varlen(const void* q8, const void* k8, const void* v8,
                                  int32_t head_dim, float softmax_scale, const void* d_state, void* out,
                                  int64_t ld_out, void* stream) {
   return attn_common(q8, k8, v8, d_cu_seqlens, num_segments, max_seqlen, total_tokens, num_heads, head_dim,
-                     softmax_scale, d_state, out, false, nullptr, ld_out, stream);
+                     softmax_scale, d_state, out, false, nullptr, ld_out, nullptr, 0, stream);
+}
+
+size_t fp8vit_attn_workspace_bytes(int32_t num_segments, int32_t max_seqlen, int32_t total_tokens,
+                                   int32_t num_heads, int32_t head_dim) {
+  if (num_segments <= 0 || max_seqlen <= 0 || total_tokens <= 0 || num_heads <= 0) return 0;
+  size_t need = 0;
+  (void)fp8vit::attn_split_plan(head_dim, num_heads, total_tokens, num_segments, max_seqlen, (size_t)-1, &need);
+  return need;
+}
+
+fp8vit_status fp8vit_attn_varlen_ws(const void* q8, const void* k8, const void* v8, const int32_t* d_cu_seqlens,
+                                    int32_t num_segments, int32_t max_seqlen, int32_t total_tokens,
+                                    int32_t num_heads, int32_t head_dim, float softmax_scale, const void* d_state,
+                                    void* out, int64_t ld_out, void* d_workspace, size_t workspace_bytes,
+                                    void* stream) {
+  return attn_common(q8, k8, v8, d_cu_seqlens, num_segments, max_seqlen, total_tokens, num_heads, head_dim,
+                     softmax_scale, d_state, out, false, nullptr, ld_out, d_workspace, workspace_bytes, stream);
 }
 
 fp8vit_status fp8vit_attn_varlen_fp8out(const void* q8, const void* k8, const void* v8,
@@ -136,7 +167,7 @@ fp8vit_status fp8vit_attn_varlen_fp8out(const void* q8, const void* k8, const vo
                                         float softmax_scale, const void* d_state, const float* d_out_descale,
                                         void* out8, int64_t ld_out8, void* stream) {
   return attn_common(q8, k8, v8, d_cu_seqlens, num_segments, max_seqlen, total_tokens, num_heads, head_dim,
-                     softmax_scale, d_state, out8, true, d_out_descale, ld_out8, stream);
+                     softmax_scale, d_state, out8, true, d_out_descale, ld_out8, nullptr, 0, stream);
 }
 
 fp8vit_status fp8vit_state_read(const void* d_state, fp8vit_state_view* out, void* stream) {

@@ -909,6 +909,127 @@ __device__ __forceinline__ void widen(const uint8_t* v8, uint8_t* vh, int wave, 
 }
 }  // namespace w32
 
+// Key split of attn_w32_kernel: a piece of a split item leaves O / l (f16),
+// m_ref and l for its queries in its record (kSplitSlotBytes per (item,
+// piece): O at [query][72], then m and l as fp32 [256] each).
+__device__ __forceinline__ void split_write_partial(const AttnArgs& a, const w32::v16f* o, float lsum, float mref,
+                                                    int item, int piece, int L, int q0, int wave, int l32, int hf) {
+  constexpr int D = 72;
+  const int ql = wave * 32 + l32;   // query within the item
+  if (q0 + ql >= L) return;
+  uint8_t* slot = a.ws_slots + ((size_t)item * a.nsplit + piece) * kSplitSlotBytes;
+  const float f = 1.0f / lsum;
+#pragma unroll
+  for (int db = 0; db < 3; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int col = 32 * db + 8 * i + 4 * hf;
+      if (col + 4 <= D) {
+        const v2h lo = {(_Float16)(o[db][4 * i] * f), (_Float16)(o[db][4 * i + 1] * f)};
+        const v2h hi = {(_Float16)(o[db][4 * i + 2] * f), (_Float16)(o[db][4 * i + 3] * f)};
+        *reinterpret_cast<uint2*>(slot + (size_t)ql * (D * 2) + col * 2) =
+            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+      }
+    }
+  if (hf == 0) {
+    float* ml = reinterpret_cast<float*>(slot + (size_t)kSplitQueries * D * 2);
+    ml[ql] = mref;
+    ml[kSplitQueries + ql] = lsum;
+  }
+}
+
+// Combine of the key split (launched after attn_w32_kernel on the same
+// stream, so every record is complete and visible): one workgroup per item,
+// two threads per query, 36 columns each. The pieces are combined in piece
+// order (deterministic):
+//   M = max_p m_p, w_p = l_p 2^(m_p - M), O = dv * sum_p w_p O_p / sum_p w_p,
+// then written as the unsplit epilogue writes (bf16, or e4m3 of O / out_descale).
+// Items that were not split (one piece) were written by the attention kernel.
+template <bool OUT8>
+__global__ __launch_bounds__(2 * kSplitQueries) void attn_split_combine_kernel(AttnArgs a) {
+  constexpr int D = 72, BM = kSplitQueries;
+  const int item = blockIdx.x;
+  const int h = item / a.ntiles_ub;
+  int tile = item - h * a.ntiles_ub;
+  if (h >= a.H) return;
+  int s0 = 0, L = -1;
+  for (int i = 0; i < a.nseg; ++i) {
+    const int b0 = a.cu[i], b1 = a.cu[i + 1];
+    const int n = (b1 - b0 + BM - 1) / BM;
+    if (tile < n) { s0 = b0; L = b1 - b0; break; }
+    tile -= n;
+  }
+  if (L <= 0) return;
+  const int q0 = tile * BM;
+  const int np = min(a.nsplit, (L + kBN - 1) / kBN);
+  if (np <= 1) return;
+  const int q = threadIdx.x >> 1, half = threadIdx.x & 1;
+  if (q0 + q >= L) return;
+  const float dv = a.st->descale_used[2];
+  const uint8_t* slots = a.ws_slots + (size_t)item * a.nsplit * kSplitSlotBytes;
+  // all m and l loads first, then all O loads: a couple of memory round trips
+  constexpr int kMaxPieces = 16;
+  float mp[kMaxPieces], lp[kMaxPieces];
+#pragma unroll
+  for (int p = 0; p < kMaxPieces; ++p) {
+    if (p < np) {
+      const float* ml = reinterpret_cast<const float*>(slots + (size_t)p * kSplitSlotBytes + (size_t)kSplitQueries * D * 2);
+      mp[p] = ml[q];
+      lp[p] = ml[kSplitQueries + q];
+    }
+  }
+  float mx = mp[0];
+#pragma unroll
+  for (int p = 1; p < kMaxPieces; ++p)
+    if (p < np) mx = fmaxf(mx, mp[p]);
+  float acc[36];
+#pragma unroll
+  for (int c = 0; c < 36; ++c) acc[c] = 0.f;
+  float den = 0.f;
+#pragma unroll
+  for (int p = 0; p < kMaxPieces; ++p) {
+    if (p < np) {
+      const float wgt = lp[p] * __builtin_amdgcn_exp2f(mp[p] - mx);
+      den += wgt;
+      const uint8_t* row = slots + (size_t)p * kSplitSlotBytes + (size_t)q * (D * 2) + half * 72;
+      uint2 raw[9];
+#pragma unroll
+      for (int c = 0; c < 9; ++c) raw[c] = *reinterpret_cast<const uint2*>(row + 8 * c);
+#pragma unroll
+      for (int c = 0; c < 9; ++c) {
+        const v2h lo = __builtin_bit_cast(v2h, raw[c].x), hi = __builtin_bit_cast(v2h, raw[c].y);
+        acc[4 * c] = fmaf(wgt, (float)lo[0], acc[4 * c]);
+        acc[4 * c + 1] = fmaf(wgt, (float)lo[1], acc[4 * c + 1]);
+        acc[4 * c + 2] = fmaf(wgt, (float)hi[0], acc[4 * c + 2]);
+        acc[4 * c + 3] = fmaf(wgt, (float)hi[1], acc[4 * c + 3]);
+      }
+    }
+  }
+  const float f = dv / den;
+  const int64_t orow = (int64_t)(s0 + q0 + q) * a.ld_out + (int64_t)h * D + 36 * half;
+  if (OUT8) {
+    const double out_rcp = 1.0 / (double)(*a.out_descale);
+#pragma unroll
+    for (int c = 0; c < 9; ++c) {
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        y[e] = __builtin_amdgcn_fmed3f((float)((double)(acc[4 * c + e] * f) * out_rcp), -kFp8Max, kFp8Max);
+      int t = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+      t = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], t, true);
+      *reinterpret_cast<int*>(a.out8 + orow + 4 * c) = t;
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 9; ++c) {
+      uint2 pk;
+      pk.x = bf16_rne(acc[4 * c] * f) | (bf16_rne(acc[4 * c + 1] * f) << 16);
+      pk.y = bf16_rne(acc[4 * c + 2] * f) | (bf16_rne(acc[4 * c + 3] * f) << 16);
+      *reinterpret_cast<uint2*>(a.out + orow + 4 * c) = pk;
+    }
+  }
+}
+
 template <bool OUT8>
 __global__ __launch_bounds__(64 * w32::WAVES) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_w32_kernel(AttnArgs a) {
@@ -921,11 +1042,13 @@ void attn_w32_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t vh_lds0[VHBUF];
   __shared__ __attribute__((aligned(1024))) uint8_t vh_lds1[VHBUF];
 
-  // ---- work item: XCD-grouped (head, query tile) -> segment by prefix scan ----
+  // ---- work item: XCD-grouped (head, query tile, key piece) -> segment by prefix scan ----
   const int G = gridDim.x;
   const int w = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-  const int h = w / a.ntiles_ub;
-  int tile = w - h * a.ntiles_ub;
+  const int item = w / a.nsplit;
+  const int piece = w - item * a.nsplit;
+  const int h = item / a.ntiles_ub;
+  int tile = item - h * a.ntiles_ub;
   if (h >= a.H) return;
   int s0 = 0, L = -1;
   for (int i = 0; i < a.nseg; ++i) {
@@ -937,6 +1060,10 @@ void attn_w32_kernel(AttnArgs a) {
   if (L <= 0) return;
   const int q0 = tile * BM;
   const int ntiles = (L + kBN - 1) / kBN;
+  // This workgroup's key tiles [ja, jb): piece `piece` of np near-equal pieces.
+  const int np = min(a.nsplit, ntiles);
+  if (piece >= np) return;
+  const int ja = (int)(((int64_t)piece * ntiles) / np), jb = (int)(((int64_t)(piece + 1) * ntiles) / np);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -971,8 +1098,8 @@ void attn_w32_kernel(AttnArgs a) {
     dma_issue<D, WAVES>(krs, vrs, dma_off, wave, (uint32_t)tk * kBN * row_stride, kdst,
                         (uint32_t)tv * kBN * row_stride, vdst, with_v);
   };
-  dma_tiles(0, k_lds0, 0, v_lds0, true);
-  dma_tiles(1, k_lds1, 1, v_lds1, true);
+  dma_tiles(ja, k_lds0, ja, v_lds0, true);
+  dma_tiles(ja + 1, k_lds1, ja + 1, v_lds1, true);
   // Rows 80..95 of the widened V^T (no V columns) stay zero: in each buffer,
   // chunks 16..23 (block db = 2), lanes with l % 32 >= 16.
   for (int r = tid; r < 2 * 256; r += 64 * WAVES) {
@@ -1011,10 +1138,10 @@ void attn_w32_kernel(AttnArgs a) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) zero16[r] = 0.f;
 
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's DMA of K(0), K(1), V(0), V(1)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's DMA of K(ja), K(ja+1), V(ja), V(ja+1)
   __syncthreads();
   const int vl_lane = v_lane_offset<D>(g, i16);
-  widen(v_lds0, vh_lds0, wave, g, i16, vl_lane);      // V(0)
+  widen(v_lds0, vh_lds0, wave, g, i16, vl_lane);      // V(ja)
 
   const int ka_lane = 16 * lane, kb_lane = 2048 + 16 * l32 + 8 * hf;
   auto k_a = [&](const lds_u8* kb, int u) -> v8i {
@@ -1024,7 +1151,7 @@ void attn_w32_kernel(AttnArgs a) {
   };
   auto k_b = [&](const lds_u8* kb, int u) -> long { return *(const lds_i64*)(kb + u * 2560 + kb_lane); };
 
-  // S(0)
+  // S(ja)
   v16f sc[4];
   {
     const lds_u8* kb = (const lds_u8*)k_lds0;
@@ -1108,12 +1235,15 @@ void attn_w32_kernel(AttnArgs a) {
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
-  int j = 0;
-  for (; j + 2 < ntiles; j += 2) {
+  // Buffer parity is relative to ja (the prologue filled buffers 0 with tile
+  // ja). The last iteration of a piece has no S(j+1); its key mask only
+  // removes keys past the segment end, so it is a no-op before the last tile.
+  int j = ja;
+  for (; j + 2 < jb; j += 2) {
     iteration(F_{}, F_{}, j);
     iteration(F_{}, T_{}, j + 1);
   }
-  if (j + 1 < ntiles) {
+  if (j + 1 < jb) {
     iteration(F_{}, F_{}, j);
     iteration(T_{}, T_{}, j + 1);
   } else {
@@ -1122,11 +1252,16 @@ void attn_w32_kernel(AttnArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no DMA in flight past the loop
 
   // ---- epilogue: row sum = O^T row 72 (block 2, register 4 of half 0) ----
+  const float lsum = __shfl(o[2][4], l32, 64);
+  const int qr = q0 + wave * 32 + l32;
+  if (np > 1) {
+    // one piece of a split item: leave its partial for attn_split_combine_kernel
+    split_write_partial(a, o, lsum, mref, item, piece, L, q0, wave, l32, hf);
+    return;
+  }
   double out_rcp = 0.0;
   if (OUT8) out_rcp = 1.0 / (double)(*a.out_descale);
-  const float lsum = __shfl(o[2][4], l32, 64);
   const float f = dv / lsum;
-  const int qr = q0 + wave * 32 + l32;
   if (qr < L) {
     const int64_t row = (int64_t)(s0 + qr) * a.ld_out + (int64_t)h * D;
 #pragma unroll
@@ -1169,6 +1304,7 @@ int64_t tiles_ub(int bm, int64_t total_tokens, int64_t nseg, int64_t max_seqlen)
 template <int D, bool WIDE>
 hipError_t launch_shape(AttnArgs a, int total_tokens, int max_seqlen, hipStream_t s) {
   a.ntiles_ub = (int32_t)tiles_ub(Shape<D, WIDE>::BM, total_tokens, a.nseg, max_seqlen);
+  a.nsplit = 1;   // the key split exists in the wide hd72 kernel only
   const int64_t items = (int64_t)a.H * a.ntiles_ub;
   const int64_t grid = ((items + 7) / 8) * 8;
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
@@ -1181,7 +1317,8 @@ hipError_t launch_shape(AttnArgs a, int total_tokens, int max_seqlen, hipStream_
 }
 hipError_t launch_w32(AttnArgs a, int total_tokens, int max_seqlen, hipStream_t s) {
   a.ntiles_ub = (int32_t)tiles_ub(w32::BM, total_tokens, a.nseg, max_seqlen);
-  const int64_t items = (int64_t)a.H * a.ntiles_ub;
+  if (a.nsplit < 1 || a.ws_slots == nullptr) a.nsplit = 1;
+  const int64_t items = (int64_t)a.H * a.ntiles_ub * a.nsplit;
   const int64_t grid = ((items + 7) / 8) * 8;
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 block(64 * w32::WAVES);
@@ -1189,9 +1326,61 @@ hipError_t launch_w32(AttnArgs a, int total_tokens, int max_seqlen, hipStream_t 
     hipLaunchKernelGGL(attn_w32_kernel<true>, dim3((unsigned)grid), block, 0, s, a);
   else
     hipLaunchKernelGGL(attn_w32_kernel<false>, dim3((unsigned)grid), block, 0, s, a);
+  if (a.nsplit == 1) return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 cgrid((unsigned)((int64_t)a.H * a.ntiles_ub)), cblock(2 * kSplitQueries);
+  if (a.out8 != nullptr)
+    hipLaunchKernelGGL(attn_split_combine_kernel<true>, cgrid, cblock, 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_split_combine_kernel<false>, cgrid, cblock, 0, s, a);
   return hipGetLastError();
 }
 }  // namespace
+
+// Key split of the wide hd72 kernel. It pays only where the grid of
+// (head, 256-query tile) items leaves CUs idle: with one workgroup per CU, a
+// grid of `items` < CUs runs in one round of nkt key tiles. Cut every item
+// into s pieces and the same work runs in ceil(items * s / CUs) rounds of
+// ceil(nkt / s) tiles, each piece paying a fixed cost (Q load, pipeline fill
+// and drain, record write) of about kSplitFixed tiles, and the combine kernel
+// about kSplitCombine tiles. Measured on MI355X (graph replays): L = 4096 at
+// 8 heads, one round of two pieces, 72.5 -> 44 us for the attention kernel;
+// L = 2304 at 16 heads, two rounds of three pieces, 43.8 -> 40 us, which the
+// combine eats. The plan takes the s with the smallest modelled time that
+// fits the workspace, and splits only if that beats the unsplit model by more
+// than 10 %. At most kSplitMaxRounds rounds, which also bounds the workspace
+// (kSplitMaxRounds * CUs partial records: 39.8 MB on 256 CUs).
+constexpr int kSplitMax = 16;   // the combine holds up to 16 pieces' m and l in registers
+constexpr int kSplitMaxRounds = 4;
+constexpr float kSplitFixed = 2.5f, kSplitCombine = 3.0f;
+
+int attn_split_plan(int head_dim, int num_heads, int total_tokens, int num_segments, int max_seqlen,
+                    size_t workspace_bytes, size_t* bytes) {
+  *bytes = 0;
+  if (head_dim != 72 || num_heads <= 0 || total_tokens <= 0 || num_segments <= 0 || max_seqlen <= 0) return 1;
+  const int cus = device_cus();
+  if (cus <= 0) return 1;
+  const int64_t items = (int64_t)num_heads * tiles_ub(w32::BM, total_tokens, num_segments, max_seqlen);
+  if (2 * items < cus || items >= cus) return 1;   // narrow kernel, or the grid already fills the chip
+  const int64_t nkt = ((int64_t)max_seqlen + kBN - 1) / kBN;
+  const float unsplit = (float)nkt + kSplitFixed;
+  int best = 1;
+  float best_cost = 0.9f * unsplit;
+  for (int sp = 2; sp <= kSplitMax && sp <= nkt; ++sp) {
+    const size_t need = (size_t)items * sp * kSplitSlotBytes;
+    if (need > workspace_bytes) break;
+    const int64_t rounds = (items * sp + cus - 1) / cus;
+    if (rounds > kSplitMaxRounds) break;
+    const float cost = (float)rounds * ((float)((nkt + sp - 1) / sp) + kSplitFixed) + kSplitCombine;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = sp;
+    }
+  }
+  if (best > 1) *bytes = (size_t)items * best * kSplitSlotBytes;
+  return best;
+}
 
 hipError_t launch_attn(const AttnArgs& a, int head_dim, int total_tokens, int max_seqlen, hipStream_t s) {
   // The wide shape once its workgroups occupy at least half of the CUs (by

@@ -77,8 +77,25 @@ struct AttnArgs {
   const float* out_descale;  // device fp32, with out8
   int64_t ld_out;          // token stride of the output, elements
   float softmax_scale;
+  // Key split (the wide hd72 kernel): every (head, query tile) item's key
+  // tiles are cut into up to nsplit pieces, one workgroup each; the pieces
+  // leave normalised partial outputs in ws_slots, and a second kernel
+  // combines them.
+  int32_t nsplit;            // 1: no split
+  uint8_t* ws_slots;         // [H * ntiles_ub * nsplit] partial records of kSplitSlotBytes
 };
-// Picks the workgroup shape and sets a.ntiles_ub for it.
+// Partial record of one key piece of a 256-query item: O / l as f16
+// [256][72], then the reference max m (log2 units) [256] and the row sum l
+// [256] as fp32.
+constexpr int kSplitQueries = 256;
+constexpr size_t kSplitSlotBytes = (size_t)kSplitQueries * 72 * 2 + 2 * kSplitQueries * 4;
+// Key split for this problem within a workspace budget: returns the number of
+// pieces per item (1: no split) and sets *bytes to the workspace it uses (0
+// with no split).
+int attn_split_plan(int head_dim, int num_heads, int total_tokens, int num_segments, int max_seqlen,
+                    size_t workspace_bytes, size_t* bytes);
+// Picks the workgroup shape and sets a.ntiles_ub for it (and the split when
+// a.ws_slots is given).
 hipError_t launch_attn(const AttnArgs& a, int head_dim, int total_tokens, int max_seqlen, hipStream_t s);
 int attn_block_m(int head_dim);
 

@@ -189,6 +189,48 @@ fp8vit_status fp8vit_attn_varlen(const void* q8, const void* k8, const void* v8,
                                  int32_t head_dim, float softmax_scale, const void* d_state,
                                  void* out, int64_t ld_out, void* stream);
 
+/* Bytes of workspace fp8vit_attn_varlen_ws uses for this problem on the
+ * current device; 0 when it would not split the keys (the grid already fills
+ * the GPU or splitting would not pay, head_dim is 128, or the problem is
+ * empty). Host only; a device property query, no launch.
+ * Source: vLLM page "FP8 ViT Encoder Attention", Performance (the MI300X
+ * AITER table's sequence lengths: at 16 heads and head_dim 72 a short
+ * sequence gives fewer (head, query tile) items than the GPU has CUs). */
+size_t fp8vit_attn_workspace_bytes(int32_t num_segments, int32_t max_seqlen, int32_t total_tokens,
+                                   int32_t num_heads, int32_t head_dim);
+
+/* fp8vit_attn_varlen with a caller workspace that lets the kernel split the
+ * keys when the grid of (head, 256-query tile) items is too small to fill the
+ * GPU (head_dim 72; for example L = 4096 at 8 heads gives 128 items for 256
+ * CUs). Each item's key tiles are cut into equal pieces, one workgroup each;
+ * the pieces write normalised partial outputs (O / l as f16, with m and l as
+ * fp32) to the workspace, and a second kernel on the same stream combines
+ * them in piece order: O = sum_p w_p O_p / sum_p w_p with
+ * w_p = l_p 2^(m_p - max m). The split is taken only where a cost model of
+ * the kernel (measured on MI355X) predicts a gain of more than 10 %; elsewhere
+ * this call is fp8vit_attn_varlen, bit for bit. The result is deterministic
+ * and invariant under segment permutation, and agrees with fp8vit_attn_varlen
+ * within the attention tolerance (not bitwise: the partials are rounded to
+ * f16).
+ *   d_workspace      device buffer, 256-byte aligned, of workspace_bytes
+ *                    bytes; its contents need no initialisation. Calls that
+ *                    share a workspace must not overlap.
+ *   workspace_bytes  its size. With less than fp8vit_attn_workspace_bytes()
+ *                    the call splits less or not at all; 0 (d_workspace may
+ *                    then be NULL) is fp8vit_attn_varlen.
+ * Other arguments, layout and errors as fp8vit_attn_varlen (also
+ * ERR_INVALID_ARGUMENT for a NULL workspace with workspace_bytes > 0, and
+ * ERR_UNSUPPORTED for a misaligned one).
+ * Source: vLLM page "FP8 ViT Encoder Attention", Requirements (varlen FP8
+ * attention with one scale per tensor) and Performance (the MI300X AITER
+ * table's sequence lengths, where smaller images give fewer query tiles). */
+fp8vit_status fp8vit_attn_varlen_ws(const void* q8, const void* k8, const void* v8,
+                                    const int32_t* d_cu_seqlens, int32_t num_segments,
+                                    int32_t max_seqlen, int32_t total_tokens, int32_t num_heads,
+                                    int32_t head_dim, float softmax_scale, const void* d_state,
+                                    void* out, int64_t ld_out, void* d_workspace,
+                                    size_t workspace_bytes, void* stream);
+
 /* fp8vit_attn_varlen with an e4m3 output, to feed an FP8 output projection
  * without a separate quantization pass (the fused fp8-output request on the
  * vLLM issue page "Add support for fused fp8 output to FlashAttention 3").
