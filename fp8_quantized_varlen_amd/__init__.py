@@ -21,7 +21,7 @@ __all__ = [
     "LIB_PATH", "FP8VIT_DYNAMIC", "FP8VIT_STATIC", "Fp8VitError",
     "state_bytes", "new_state", "state_init", "state_set_static", "scales_update",
     "quantize_qkv", "attn_varlen", "attn_varlen_fp8out", "attn_workspace_bytes", "attn_workspace",
-    "attn_varlen_ws", "state_read", "state_write", "calibrated_values",
+    "attn_varlen_ws", "attn_varlen_noalloc", "state_read", "state_write", "calibrated_values",
     "load_static_scales", "save_static_scales", "status_str",
 ]
 
@@ -52,6 +52,8 @@ _SIGS = {
     "fp8vit_attn_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32, _i32]),
     "fp8vit_attn_varlen_ws": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
                                              _vp, _i64, _vp, ctypes.c_size_t, _vp]),
+    "fp8vit_attn_varlen_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
+                                                  _vp, _i64, _vp]),
     "fp8vit_state_read": (ctypes.c_int, [_vp, ctypes.POINTER(_StateView), _vp]),
     "fp8vit_state_write": (ctypes.c_int, [_vp, ctypes.POINTER(_StateView), _vp]),
     "fp8vit_calibrated_values": (ctypes.c_int, [_vp, _f32, ctypes.POINTER(_f32), _vp]),
@@ -293,6 +295,26 @@ def attn_varlen_ws(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, cu_seql
                                     int(max_seqlen), T, H, d, float(softmax_scale), _ptr(state), _ptr(out), ld_out,
                                     _ptr(workspace), workspace.numel(), _stream(dev))
     _check("fp8vit_attn_varlen_ws", st)
+    return out
+
+
+def attn_varlen_noalloc(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, cu_seqlens: torch.Tensor,
+                        max_seqlen: int, state: torch.Tensor, softmax_scale: float = 0.0,
+                        out: torch.Tensor = None) -> torch.Tensor:
+    """attn_varlen_ws with the library's own static workspace: the library allocates nothing
+    (pass `out` to allocate nothing here either). Calls that overlap on one GPU race."""
+    q8, k8, v8, cu_seqlens, state = _attn_inputs(q8, k8, v8, cu_seqlens, max_seqlen, state)
+    T, H, d = q8.shape
+    if out is not None:
+        out = _bhd("out", out, (torch.bfloat16,), shape=q8.shape)
+    dev = _same_gpu(q8=q8, k8=k8, v8=v8, cu_seqlens=cu_seqlens, state=state, out=out)
+    if out is None:
+        out = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+    ld_out = out.stride(0) if T > 0 else H * d
+    st = _lib.fp8vit_attn_varlen_noalloc(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(cu_seqlens), cu_seqlens.numel() - 1,
+                                         int(max_seqlen), T, H, d, float(softmax_scale), _ptr(state), _ptr(out),
+                                         ld_out, _stream(dev))
+    _check("fp8vit_attn_varlen_noalloc", st)
     return out
 
 

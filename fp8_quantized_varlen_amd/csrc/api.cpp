@@ -81,7 +81,7 @@ fp8vit_status attn_common(const void* q8, const void* k8, const void* v8, const 
                           int32_t num_segments, int32_t max_seqlen, int32_t total_tokens, int32_t num_heads,
                           int32_t head_dim, float softmax_scale, const void* d_state, void* out, bool out_fp8,
                           const float* d_out_descale, int64_t ld_out, void* d_workspace, size_t workspace_bytes,
-                          void* stream) {
+                          bool library_scratch, void* stream) {
   if (workspace_bytes > 0 && (!d_workspace || !aligned(d_workspace, 256)))
     return d_workspace ? FP8VIT_ERR_UNSUPPORTED : FP8VIT_ERR_INVALID_ARGUMENT;
   if (!d_cu_seqlens || !d_state) return FP8VIT_ERR_INVALID_ARGUMENT;
@@ -123,6 +123,18 @@ fp8vit_status attn_common(const void* q8, const void* k8, const void* v8, const 
   a.softmax_scale = softmax_scale > 0.0f ? softmax_scale : (float)(1.0 / std::sqrt((double)head_dim));
   a.nsplit = 1;
   a.ws_slots = nullptr;
+  if (library_scratch) {
+    // The library's own workspace: take the plan the caller's workspace would
+    // get, and refuse a problem whose plan does not fit.
+    size_t need = 0;
+    (void)fp8vit::attn_split_plan(head_dim, num_heads, total_tokens, num_segments, max_seqlen, (size_t)-1, &need);
+    if (need > fp8vit::kNoAllocScratchBytes) return FP8VIT_ERR_UNSUPPORTED;
+    if (need > 0) {
+      const hipError_t e = fp8vit::noalloc_scratch(&d_workspace);
+      if (e != hipSuccess) return FP8VIT_ERR_HIP;
+      workspace_bytes = fp8vit::kNoAllocScratchBytes;
+    }
+  }
   if (workspace_bytes > 0) {
     size_t need = 0;
     const int sp = fp8vit::attn_split_plan(head_dim, num_heads, total_tokens, num_segments, max_seqlen,
@@ -141,7 +153,7 @@ fp8vit_status fp8vit_attn_varlen(const void* q8, const void* k8, const void* v8,
                                  int32_t head_dim, float softmax_scale, const void* d_state, void* out,
                                  int64_t ld_out, void* stream) {
   return attn_common(q8, k8, v8, d_cu_seqlens, num_segments, max_seqlen, total_tokens, num_heads, head_dim,
-                     softmax_scale, d_state, out, false, nullptr, ld_out, nullptr, 0, stream);
+                     softmax_scale, d_state, out, false, nullptr, ld_out, nullptr, 0, false, stream);
 }
 
 size_t fp8vit_attn_workspace_bytes(int32_t num_segments, int32_t max_seqlen, int32_t total_tokens,
@@ -158,7 +170,17 @@ fp8vit_status fp8vit_attn_varlen_ws(const void* q8, const void* k8, const void* 
                                     void* out, int64_t ld_out, void* d_workspace, size_t workspace_bytes,
                                     void* stream) {
   return attn_common(q8, k8, v8, d_cu_seqlens, num_segments, max_seqlen, total_tokens, num_heads, head_dim,
-                     softmax_scale, d_state, out, false, nullptr, ld_out, d_workspace, workspace_bytes, stream);
+                     softmax_scale, d_state, out, false, nullptr, ld_out, d_workspace, workspace_bytes, false,
+                     stream);
+}
+
+fp8vit_status fp8vit_attn_varlen_noalloc(const void* q8, const void* k8, const void* v8,
+                                         const int32_t* d_cu_seqlens, int32_t num_segments, int32_t max_seqlen,
+                                         int32_t total_tokens, int32_t num_heads, int32_t head_dim,
+                                         float softmax_scale, const void* d_state, void* out, int64_t ld_out,
+                                         void* stream) {
+  return attn_common(q8, k8, v8, d_cu_seqlens, num_segments, max_seqlen, total_tokens, num_heads, head_dim,
+                     softmax_scale, d_state, out, false, nullptr, ld_out, nullptr, 0, true, stream);
 }
 
 fp8vit_status fp8vit_attn_varlen_fp8out(const void* q8, const void* k8, const void* v8,
@@ -167,7 +189,7 @@ fp8vit_status fp8vit_attn_varlen_fp8out(const void* q8, const void* k8, const vo
                                         float softmax_scale, const void* d_state, const float* d_out_descale,
                                         void* out8, int64_t ld_out8, void* stream) {
   return attn_common(q8, k8, v8, d_cu_seqlens, num_segments, max_seqlen, total_tokens, num_heads, head_dim,
-                     softmax_scale, d_state, out8, true, d_out_descale, ld_out8, nullptr, 0, stream);
+                     softmax_scale, d_state, out8, true, d_out_descale, ld_out8, nullptr, 0, false, stream);
 }
 
 fp8vit_status fp8vit_state_read(const void* d_state, fp8vit_state_view* out, void* stream) {

@@ -37,6 +37,7 @@
 //    instead of 128.
 //  * Work items are (head, query tile); consecutive items of one head are
 //    mapped to the same XCD so that K/V re-reads hit that XCD's L2.
+#include <atomic>
 #include <type_traits>
 
 #include "fp8vit_internal.h"
@@ -1291,6 +1292,33 @@ void attn_w32_kernel(AttnArgs a) {
 }
 
 int attn_block_m(int head_dim) { return head_dim == 72 ? Shape<72, false>::BM : Shape<128, false>::BM; }
+
+// Library-owned workspace of the key split for callers that cannot allocate
+// (fp8vit_attn_varlen_noalloc). One copy per GPU, held until the process
+// ends; every call on that GPU shares it (overlapping calls race). The split
+// records need no initial contents. In host code `scratch` names a host-side
+// stand-in: kernels get the device address from hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  void* p = (dev >= 0 && dev < kMaxScratchDevices) ? g_scratch_ptr[dev].load(std::memory_order_relaxed) : nullptr;
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    if (dev >= 0 && dev < kMaxScratchDevices) g_scratch_ptr[dev].store(p, std::memory_order_relaxed);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 namespace {
 // Upper bound on query tiles of BM rows per head: every segment adds at most

@@ -94,6 +94,12 @@ constexpr size_t kSplitSlotBytes = (size_t)kSplitQueries * 72 * 2 + 2 * kSplitQu
 // with no split).
 int attn_split_plan(int head_dim, int num_heads, int total_tokens, int num_segments, int max_seqlen,
                     size_t workspace_bytes, size_t* bytes);
+// Size of the library-owned split workspace of fp8vit_attn_varlen_noalloc:
+// every plan (at most 4 rounds of one piece per CU) fits on up to 269 CUs.
+constexpr size_t kNoAllocScratchBytes = (size_t)40 << 20;
+// Device address of that workspace on the current device (looked up once per
+// device with hipGetSymbolAddress).
+hipError_t noalloc_scratch(void** ptr);
 // Picks the workgroup shape and sets a.ntiles_ub for it (and the split when
 // a.ws_slots is given).
 hipError_t launch_attn(const AttnArgs& a, int head_dim, int total_tokens, int max_seqlen, hipStream_t s);

@@ -231,6 +231,27 @@ fp8vit_status fp8vit_attn_varlen_ws(const void* q8, const void* k8, const void* 
                                     void* out, int64_t ld_out, void* d_workspace,
                                     size_t workspace_bytes, void* stream);
 
+/* fp8vit_attn_varlen_ws for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the key split's workspace is the library's own, a 40 MiB
+ * static device array per GPU that each GPU the library runs on holds until
+ * the process ends. The call itself allocates nothing (no hipMalloc, no
+ * allocating library routine); the first call on a device looks the array's
+ * address up once. The split plan, kernels and result are those of
+ * fp8vit_attn_varlen_ws with a workspace of fp8vit_attn_workspace_bytes();
+ * the array needs no initial contents and keeps the last call's partials.
+ * All calls on one GPU share the array: calls that overlap on one GPU (two
+ * streams, two threads) race and must be serialised by the caller.
+ * Arguments, layout and errors as fp8vit_attn_varlen, and ERR_UNSUPPORTED when
+ * the split this problem would take needs more than the 40 MiB (at most four
+ * rounds of one piece per CU: never on GPUs of up to 269 CUs).
+ * Source: for callers that cannot allocate (no page defines this entry). */
+fp8vit_status fp8vit_attn_varlen_noalloc(const void* q8, const void* k8, const void* v8,
+                                         const int32_t* d_cu_seqlens, int32_t num_segments,
+                                         int32_t max_seqlen, int32_t total_tokens, int32_t num_heads,
+                                         int32_t head_dim, float softmax_scale, const void* d_state,
+                                         void* out, int64_t ld_out, void* stream);
+
 /* fp8vit_attn_varlen with an e4m3 output, to feed an FP8 output projection
  * without a separate quantization pass (the fused fp8-output request on the
  * vLLM issue page "Add support for fused fp8 output to FlashAttention 3").
