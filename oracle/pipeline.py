@@ -14,7 +14,7 @@ from typing import Optional
 
 import numpy as np
 
-from . import quant, scales, attention
+from . import quant, scales, attention, mx
 
 
 @dataclass
@@ -70,3 +70,35 @@ def calibrate(draws, margin: float = 1.5) -> np.ndarray:
     for (q, k, v) in draws:
         ring.push([quant.amax(q), quant.amax(k), quant.amax(v)])
     return scales.calibrated_values(ring, margin)
+
+
+@dataclass
+class MxForwardResult:
+    q: tuple                # (e4m3 codes uint8 [T, H, d], E8M0 scales uint8 [T, H, 4])
+    k: tuple
+    v_codes: np.ndarray     # per-tensor e4m3 codes of V
+    v_descale: np.float32
+    out: Optional[np.ndarray]
+
+
+def forward_mx(q, k, v, cu_seqlens, mode: str, ring: Optional[scales.AmaxRing] = None, static_values=None,
+               softmax_scale=None, attend: bool = True) -> MxForwardResult:
+    """Block-scaled variant: Q and K quantized with one power-of-two scale per
+    32-element block of head_dim (oracle.mx, readings R25-R27), V with its
+    per-tensor scale as in forward() (R28: dynamic ring or static value), then
+    the same fp64 attention over the dequantized values."""
+    qc, qs = mx.quantize(q)
+    kc, ks = mx.quantize(k)
+    if mode == "dynamic":
+        a = np.array([quant.amax(q), quant.amax(k), quant.amax(v)], dtype=np.float32)
+        dv = scales.dynamic_descales(ring, a)[2]
+    elif mode == "static":
+        dv = scales.static_descales(static_values)[2]
+    else:
+        raise ValueError(mode)
+    vc = quant.quantize(v, dv)
+    out = None
+    if attend:
+        out = attention.attention(mx.dequantize(qc, qs), mx.dequantize(kc, ks), quant.dequantize(vc, dv),
+                                  cu_seqlens, softmax_scale)
+    return MxForwardResult((qc, qs), (kc, ks), vc, np.float32(dv), out)
