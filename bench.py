@@ -58,6 +58,9 @@ def parse():
                    help="q,k,v static values to use instead of calibrating (profiling runs: no dynamic passes)")
     p.add_argument("--out", choices=("bf16", "fp8"), default="bf16",
                    help="attention output: bf16, or e4m3 with a static output descale (fused fp8 output)")
+    p.add_argument("--scaling", choices=("tensor", "mx"), default="tensor",
+                   help="tensor: per-tensor scales (the method); mx: block-scaled Q and K (E8M0 scale per "
+                        "32-element block of head_dim), per-tensor V")
     p.add_argument("--graph", action="store_true",
                    help="also time the steps as one captured HIP graph (no host launch gaps)")
     p.add_argument("--hot", action="store_true",
@@ -92,7 +95,7 @@ def calibrate_static(fv, w, dev, margin=1.5):
     return [float(x) for x in loaded]
 
 
-def cpu_baseline(w, qb, kb, vb, static_values, out_gpu, target_s, compare=True):
+def cpu_baseline(w, qb, kb, vb, static_values, out_gpu, target_s, compare=True, mx=False):
     """The oracle, untuned, timed on this host: oracle quantization of Q, K and V
     plus fp64 oracle attention. Whole steps are repeated until about `target_s`
     seconds of CPU work are done; a workload whose single step would take more
@@ -113,6 +116,11 @@ def cpu_baseline(w, qb, kb, vb, static_values, out_gpu, target_s, compare=True):
 
     def quantize():
         ring = oracle.scales.AmaxRing()
+        if mx:
+            r = oracle.pipeline.forward_mx(qb, kb, vb, None, w.mode, ring=ring, static_values=static_values,
+                                           attend=False)
+            return [oracle.mx.dequantize(*r.q), oracle.mx.dequantize(*r.k),
+                    oracle.quant.dequantize(r.v_codes, r.v_descale)]
         codes, ds, _ = oracle.pipeline.quantize_step(qb, kb, vb, w.mode, ring=ring, static_values=static_values)
         return [oracle.quant.dequantize(c, dd) for c, dd in zip(codes, ds)]
 
@@ -184,20 +192,23 @@ def cpu_baseline(w, qb, kb, vb, static_values, out_gpu, target_s, compare=True):
             "gpu_rows_checked": int(sum(n for _, _, n, _, _ in rows_out))}
 
 
-def attn_kernel_name(w, dev, out8):
+def attn_kernel_name(w, dev, out8, mx=False):
     """Name of the attention kernel instance the library launches for this
     workload, as the profiler prints it: the wide shape (256 queries per
     workgroup) is used once its workgroups cover at least half of the CUs; at
-    head dim 72 it is the 32x32-block kernel attn_w32_kernel."""
+    head dim 72 it is the 32x32-block kernel attn_w32_kernel, except with
+    block-scaled Q and K (mx), which run the narrow hd72 shape."""
     import torch
     d = w.head_dim
     T, nseg, L = w.total_tokens, len(w.seglens), max(w.seglens)
     tiles = min((T + 255) // 256 + nseg, nseg * ((L + 255) // 256))
     wide = 2 * w.heads * tiles >= torch.cuda.get_device_properties(dev).multi_processor_count
     o8 = "true" if out8 else "false"
+    if mx:
+        return "attn_kernel<%d, false, %s, true>" % (d, "true" if wide and d == 128 else "false")
     if wide and d == 72:
         return "attn_w32_kernel<%s>" % o8
-    return "attn_kernel<%d, %s, %s>" % (d, o8, "true" if wide else "false")
+    return "attn_kernel<%d, %s, %s, false>" % (d, o8, "true" if wide else "false")
 
 
 def attn_traffic(workload, head_dim):
@@ -353,8 +364,22 @@ def main():
     ws_bytes = fv.attn_workspace_bytes(len(w.seglens), max_seqlen, T, H, d)
     ws = fv.attn_workspace(len(w.seglens), max_seqlen, T, H, d, device=dev)
 
+    mx = args.scaling == "mx"
+    if mx and out8 is not None:
+        print("--scaling mx has no fp8 output variant", file=sys.stderr)
+        sys.exit(2)
+    qs, ks = (torch.empty((T, H, 4), dtype=torch.uint8, device=dev) for _ in range(2))
+
+    def quantize(q, k, v):
+        if mx:
+            fv.quantize_qkv_mx(q, k, v, st, w.mode, out=(q8, k8, v8, qs, ks))
+        else:
+            fv.quantize_qkv(q, k, v, st, w.mode, out=(q8, k8, v8))
+
     def attend():
-        if out8 is not None:
+        if mx:
+            fv.attn_varlen_mx(q8, k8, v8, qs, ks, cu, max_seqlen, st, out=out)
+        elif out8 is not None:
             fv.attn_varlen_fp8out(q8, k8, v8, cu, max_seqlen, st, out_descale, out=out8)
         else:
             fv.attn_varlen_ws(q8, k8, v8, cu, max_seqlen, st, ws, out=out)
@@ -362,7 +387,7 @@ def main():
 
     def step(i):
         q, k, v = sets[i % n_sets]
-        fv.quantize_qkv(q, k, v, st, w.mode, out=(q8, k8, v8))
+        quantize(q, k, v)
         attend()
 
     clock = ClockSampler(dev.index or 0)
@@ -398,7 +423,7 @@ def main():
         e = ev.get(i)
         if e:
             e[0].record()
-        fv.quantize_qkv(q, k, v, st, w.mode, out=(q8, k8, v8))
+        quantize(q, k, v)
         if e:
             e[1].record()
         attend()
@@ -427,7 +452,7 @@ def main():
             q, k, v = sets[i % n_sets]
             if i == mid:
                 e[0].record()
-            fv.quantize_qkv(q, k, v, st, w.mode, out=(q8, k8, v8))
+            quantize(q, k, v)
             if i == mid:
                 e[1].record()
             attend()
@@ -448,13 +473,13 @@ def main():
     if args.hot:
         q, k, v = sets[0]
         for _ in range(10):
-            fv.quantize_qkv(q, k, v, st, w.mode, out=(q8, k8, v8))
+            quantize(q, k, v)
             attend()
         torch.cuda.synchronize()
         h0, h1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         h0.record()
         for _ in range(args.steps):
-            fv.quantize_qkv(q, k, v, st, w.mode, out=(q8, k8, v8))
+            quantize(q, k, v)
             attend()
         h1.record()
         torch.cuda.synchronize()
@@ -492,7 +517,7 @@ def main():
     assert not torch.isnan(out).any().item()
     state = fv.state_read(st)
 
-    kname = attn_kernel_name(w, dev, args.out == "fp8")
+    kname = attn_kernel_name(w, dev, args.out == "fp8", mx)
     value = w.flops / (ms_step * 1e-3) / 1e12
     attn_tflops = w.flops / (attn_ms * 1e-3) / 1e12
     quant_bytes = 3 * T * H * d * 3
@@ -509,11 +534,14 @@ def main():
         "vs_baseline": round(value / PAGE_MI300X_TFLOPS[w.name], 3) if w.name in PAGE_MI300X_TFLOPS else None,
         # S = Q K^T on the FP8 MFMA; P.V on the f16 MFMA in the wide kernels,
         # on the FP8 MFMA (two e4m3 terms of P) in the narrow ones
-        "dtype": "fp8e4m3+f16" if kname.startswith("attn_w32") or kname.endswith(", true>") else "fp8e4m3",
+        "dtype": ("fp8e4m3+f16" if kname.startswith("attn_w32") or
+                  (kname.startswith("attn_kernel<128") and kname.split(", ")[2] == "true")
+                  else "fp8e4m3") + ("+e8m0 block scales (Q, K)" if mx else ""),
         "data": "synthetic",
         "config": {"workload": w.name, "segments": list(w.seglens), "heads": H, "head_dim": d, "output": args.out,
-                   "key_split_workspace_bytes": ws_bytes if out8 is None else 0,
-                   "scaling": w.mode + (" (1.5 x calibrated)" if w.mode == "static" else " (16-slot ring)"),
+                   "key_split_workspace_bytes": ws_bytes if out8 is None and not mx else 0,
+                   "scaling": ("Q, K: E8M0 per 32-element block; V: " if mx else "") + w.mode +
+                              (" (1.5 x calibrated)" if w.mode == "static" else " (16-slot ring)"),
                    "outlier_frac": w.outlier_frac, "input_sets_rotated": n_sets},
         "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
         "settle": {"seconds": round(settle_s, 3), "steps": settle_steps},
@@ -535,7 +563,7 @@ def main():
                     "attention_TFLOPs": round(attn_tflops, 2)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4),
-                     "traffic": attn_traffic(w.name, d),
+                     "traffic": None if mx else attn_traffic(w.name, d),
                      "kernel": kname},
         "descale_used": state["descale_used"],
         **({"graph": {"ms_per_step": round(graph_ms, 4),
@@ -554,7 +582,7 @@ def main():
         # dynamic mode: the GPU ring holds only this input's amax (the scales the oracle's
         # fresh ring gives) once 16 forwards of it have been pushed
         same_scales = w.mode == "static" or args.warmup + args.steps >= 16
-        res["cpu_baseline"] = cpu_baseline(w, qb, kb, vb, static_values, out_np, args.cpu_seconds, same_scales)
+        res["cpu_baseline"] = cpu_baseline(w, qb, kb, vb, static_values, out_np, args.cpu_seconds, same_scales, mx)
     print(json.dumps(res), flush=True)
 
 

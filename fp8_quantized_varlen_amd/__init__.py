@@ -21,7 +21,7 @@ __all__ = [
     "LIB_PATH", "FP8VIT_DYNAMIC", "FP8VIT_STATIC", "Fp8VitError",
     "state_bytes", "new_state", "state_init", "state_set_static", "scales_update",
     "quantize_qkv", "attn_varlen", "attn_varlen_fp8out", "attn_workspace_bytes", "attn_workspace",
-    "attn_varlen_ws", "attn_varlen_noalloc", "state_read", "state_write", "calibrated_values",
+    "attn_varlen_ws", "attn_varlen_noalloc", "quantize_qkv_mx", "attn_varlen_mx", "state_read", "state_write", "calibrated_values",
     "load_static_scales", "save_static_scales", "status_str",
 ]
 
@@ -50,6 +50,10 @@ _SIGS = {
     "fp8vit_attn_varlen_fp8out": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
                                                  _vp, _vp, _i64, _vp]),
     "fp8vit_attn_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32, _i32]),
+    "fp8vit_quantize_qkv_mx": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32,
+                                              _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "fp8vit_attn_varlen_mx": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32,
+                                             _vp, _vp, _i64, _vp]),
     "fp8vit_attn_varlen_ws": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
                                              _vp, _i64, _vp, ctypes.c_size_t, _vp]),
     "fp8vit_attn_varlen_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
@@ -315,6 +319,64 @@ def attn_varlen_noalloc(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, cu
                                          int(max_seqlen), T, H, d, float(softmax_scale), _ptr(state), _ptr(out),
                                          ld_out, _stream(dev))
     _check("fp8vit_attn_varlen_noalloc", st)
+    return out
+
+
+def _mx_scales(name, t, shape):
+    t = _tensor(name, t)
+    if t.dtype != torch.uint8 or tuple(t.shape) != (shape[0], shape[1], 4) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous uint8 tensor of shape ({shape[0]}, {shape[1]}, 4)")
+    return t
+
+
+def quantize_qkv_mx(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state: torch.Tensor, mode="dynamic",
+                    out=None):
+    """Block-scaled Q and K (e4m3 codes + E8M0 scales [T, H, 4] per 32-element block of
+    head_dim), per-tensor V: returns (q8, k8, v8, q_scales, k_scales)."""
+    q = _bhd("q", q, (torch.bfloat16,))
+    k = _bhd("k", k, (torch.bfloat16,), shape=q.shape)
+    v = _bhd("v", v, (torch.bfloat16,), shape=q.shape)
+    T, H, d = q.shape
+    state = _state_tensor(state)
+    if mode not in _MODES and mode not in (FP8VIT_DYNAMIC, FP8VIT_STATIC):
+        raise ValueError(f"mode must be 'dynamic' or 'static', got {mode!r}")
+    if out is not None:
+        if not isinstance(out, (tuple, list)) or len(out) != 5:
+            raise ValueError("out must be a tuple (q8, k8, v8, q_scales, k_scales)")
+        out = tuple(_bhd(n, o, _CODE_DTYPES, shape=q.shape, contiguous=True)
+                    for n, o in zip(("q8", "k8", "v8"), out[:3])) + tuple(
+            _mx_scales(n, o, q.shape) for n, o in zip(("q_scales", "k_scales"), out[3:]))
+    dev = _same_gpu(q=q, k=k, v=v, state=state,
+                    **({} if out is None else dict(zip(("q8", "k8", "v8", "q_scales", "k_scales"), out))))
+    if out is None:
+        out = tuple(torch.empty((T, H, d), dtype=torch.uint8, device=dev) for _ in range(3)) + tuple(
+            torch.empty((T, H, 4), dtype=torch.uint8, device=dev) for _ in range(2))
+    m = _MODES[mode] if isinstance(mode, str) else int(mode)
+    st = _lib.fp8vit_quantize_qkv_mx(_ptr(q), _ptr(k), _ptr(v), _token_stride(q), _token_stride(k), _token_stride(v),
+                                     T, H, d, m, *(_ptr(o) for o in out), _ptr(state), _stream(dev))
+    _check("fp8vit_quantize_qkv_mx", st)
+    return out
+
+
+def attn_varlen_mx(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_scales: torch.Tensor,
+                   k_scales: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int, state: torch.Tensor,
+                   softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Attention on block-scaled Q and K (from quantize_qkv_mx); bf16 [T, H, d]."""
+    q8, k8, v8, cu_seqlens, state = _attn_inputs(q8, k8, v8, cu_seqlens, max_seqlen, state)
+    T, H, d = q8.shape
+    q_scales = _mx_scales("q_scales", q_scales, q8.shape)
+    k_scales = _mx_scales("k_scales", k_scales, q8.shape)
+    if out is not None:
+        out = _bhd("out", out, (torch.bfloat16,), shape=q8.shape)
+    dev = _same_gpu(q8=q8, k8=k8, v8=v8, q_scales=q_scales, k_scales=k_scales, cu_seqlens=cu_seqlens, state=state,
+                    out=out)
+    if out is None:
+        out = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+    ld_out = out.stride(0) if T > 0 else H * d
+    st = _lib.fp8vit_attn_varlen_mx(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scales), _ptr(k_scales), _ptr(cu_seqlens),
+                                    cu_seqlens.numel() - 1, int(max_seqlen), T, H, d, float(softmax_scale),
+                                    _ptr(state), _ptr(out), ld_out, _stream(dev))
+    _check("fp8vit_attn_varlen_mx", st)
     return out
 
 

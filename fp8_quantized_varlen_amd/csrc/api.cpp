@@ -43,9 +43,14 @@ fp8vit_status fp8vit_scales_update(void* d_state, const float* d_amax_qkv, void*
   return from_hip(fp8vit::launch_scales_update(static_cast<DevState*>(d_state), d_amax_qkv, as_stream(stream)));
 }
 
-fp8vit_status fp8vit_quantize_qkv(const void* q, const void* k, const void* v, int64_t ld_q, int64_t ld_k,
-                                  int64_t ld_v, int32_t total_tokens, int32_t num_heads, int32_t head_dim,
-                                  int32_t mode, void* q8, void* k8, void* v8, void* d_state, void* stream) {
+namespace {
+
+// Validation and launch of the per-tensor quantize passes; quant_mask selects
+// which of Q, K, V (bits 0, 1, 2) get codes. Dynamic mode's amax pass and ring
+// bookkeeping always cover all three tensors.
+fp8vit_status quantize_common(const void* q, const void* k, const void* v, int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                              int32_t total_tokens, int32_t num_heads, int32_t head_dim, int32_t mode, void* q8,
+                              void* k8, void* v8, void* d_state, uint32_t quant_mask, void* stream) {
   if (!d_state || total_tokens < 0 || num_heads <= 0 || head_dim <= 0) return FP8VIT_ERR_INVALID_ARGUMENT;
   // Empty tensors may come with null data pointers; the kernel then reads nothing.
   if (total_tokens > 0 && (!q || !k || !v || !q8 || !k8 || !v8)) return FP8VIT_ERR_INVALID_ARGUMENT;
@@ -71,8 +76,39 @@ fp8vit_status fp8vit_quantize_qkv(const void* q, const void* k, const void* v, i
   a.T = total_tokens;
   a.row8 = (int32_t)(row / 8);
   a.amax_blocks = 0;
+  a.quant_mask = quant_mask;
   a.st = static_cast<DevState*>(d_state);
   return from_hip(fp8vit::launch_quantize(a, mode == FP8VIT_DYNAMIC, as_stream(stream)));
+}
+
+}  // namespace
+
+fp8vit_status fp8vit_quantize_qkv(const void* q, const void* k, const void* v, int64_t ld_q, int64_t ld_k,
+                                  int64_t ld_v, int32_t total_tokens, int32_t num_heads, int32_t head_dim,
+                                  int32_t mode, void* q8, void* k8, void* v8, void* d_state, void* stream) {
+  return quantize_common(q, k, v, ld_q, ld_k, ld_v, total_tokens, num_heads, head_dim, mode, q8, k8, v8, d_state, 7u,
+                         stream);
+}
+
+fp8vit_status fp8vit_quantize_qkv_mx(const void* q, const void* k, const void* v, int64_t ld_q, int64_t ld_k,
+                                     int64_t ld_v, int32_t total_tokens, int32_t num_heads, int32_t head_dim,
+                                     int32_t mode, void* q8, void* k8, void* v8, void* q_scales, void* k_scales,
+                                     void* d_state, void* stream) {
+  if (total_tokens > 0 && (!q_scales || !k_scales)) return FP8VIT_ERR_INVALID_ARGUMENT;
+  if (head_dim != 72 && head_dim != 128) return FP8VIT_ERR_UNSUPPORTED;
+  if (!aligned(q_scales, 4) || !aligned(k_scales, 4)) return FP8VIT_ERR_UNSUPPORTED;
+  // V (and, in dynamic mode, the amax ring of Q, K and V) as fp8vit_quantize_qkv
+  // does; Q and K then get the block-scaled codes.
+  const fp8vit_status st = quantize_common(q, k, v, ld_q, ld_k, ld_v, total_tokens, num_heads, head_dim, mode, q8,
+                                           k8, v8, d_state, 4u, stream);
+  if (st != FP8VIT_OK || total_tokens == 0) return st;
+  hipError_t e = fp8vit::launch_quantize_mx(static_cast<const uint16_t*>(q), ld_q, total_tokens, num_heads, head_dim,
+                                            static_cast<uint8_t*>(q8), static_cast<uint8_t*>(q_scales),
+                                            as_stream(stream));
+  if (e != hipSuccess) return FP8VIT_ERR_HIP;
+  e = fp8vit::launch_quantize_mx(static_cast<const uint16_t*>(k), ld_k, total_tokens, num_heads, head_dim,
+                                 static_cast<uint8_t*>(k8), static_cast<uint8_t*>(k_scales), as_stream(stream));
+  return from_hip(e);
 }
 
 namespace {
@@ -81,7 +117,8 @@ fp8vit_status attn_common(const void* q8, const void* k8, const void* v8, const 
                           int32_t num_segments, int32_t max_seqlen, int32_t total_tokens, int32_t num_heads,
                           int32_t head_dim, float softmax_scale, const void* d_state, void* out, bool out_fp8,
                           const float* d_out_descale, int64_t ld_out, void* d_workspace, size_t workspace_bytes,
-                          bool library_scratch, void* stream) {
+                          bool library_scratch, void* stream, const void* q_scales = nullptr,
+                          const void* k_scales = nullptr) {
   if (workspace_bytes > 0 && (!d_workspace || !aligned(d_workspace, 256)))
     return d_workspace ? FP8VIT_ERR_UNSUPPORTED : FP8VIT_ERR_INVALID_ARGUMENT;
   if (!d_cu_seqlens || !d_state) return FP8VIT_ERR_INVALID_ARGUMENT;
@@ -121,6 +158,8 @@ fp8vit_status attn_common(const void* q8, const void* k8, const void* v8, const 
   a.out_descale = d_out_descale;
   a.ld_out = ld_out;
   a.softmax_scale = softmax_scale > 0.0f ? softmax_scale : (float)(1.0 / std::sqrt((double)head_dim));
+  a.qs = static_cast<const uint8_t*>(q_scales);
+  a.ks = static_cast<const uint8_t*>(k_scales);
   a.nsplit = 1;
   a.ws_slots = nullptr;
   if (library_scratch) {
@@ -181,6 +220,21 @@ fp8vit_status fp8vit_attn_varlen_noalloc(const void* q8, const void* k8, const v
                                          void* stream) {
   return attn_common(q8, k8, v8, d_cu_seqlens, num_segments, max_seqlen, total_tokens, num_heads, head_dim,
                      softmax_scale, d_state, out, false, nullptr, ld_out, nullptr, 0, true, stream);
+}
+
+fp8vit_status fp8vit_attn_varlen_mx(const void* q8, const void* k8, const void* v8, const void* d_q_scales,
+                                    const void* d_k_scales, const int32_t* d_cu_seqlens, int32_t num_segments,
+                                    int32_t max_seqlen, int32_t total_tokens, int32_t num_heads, int32_t head_dim,
+                                    float softmax_scale, const void* d_state, void* out, int64_t ld_out,
+                                    void* stream) {
+  if (total_tokens > 0 && num_segments > 0 && (!d_q_scales || !d_k_scales)) return FP8VIT_ERR_INVALID_ARGUMENT;
+  if (!aligned(d_q_scales, 4) || !aligned(d_k_scales, 4)) return FP8VIT_ERR_UNSUPPORTED;
+  // Empty problems return before any launch; otherwise the non-null scales
+  // select the block-scaled kernels. The (T + 2 tiles) * H scale dwords stay
+  // far below the 31-bit offsets the code tensors are bounded by.
+  return attn_common(q8, k8, v8, d_cu_seqlens, num_segments, max_seqlen, total_tokens, num_heads, head_dim,
+                     softmax_scale, d_state, out, false, nullptr, ld_out, nullptr, 0, false, stream, d_q_scales,
+                     d_k_scales);
 }
 
 fp8vit_status fp8vit_attn_varlen_fp8out(const void* q8, const void* k8, const void* v8,

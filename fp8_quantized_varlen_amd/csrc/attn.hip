@@ -142,16 +142,32 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
 
 // A operand of S^T block t (see the K placement above). `kl` is the lane's
 // byte offset for t = 0 (k_lane_offset).
-template <int D>
+//  MX (block scales): the scaled MFMA takes the scale of K positions
+//     32 j .. 32 j + 31 from lane group j, while lane group g's operand holds
+//     positions 16 g .. 16 g + 15 (low four dwords) and 64 + 16 g .. + 15
+//     (high four). So the MX operands hold d in that natural order: the low
+//     chunk is d bytes 16 g .., the high chunk d bytes 64 + 16 g .. (hd72:
+//     only lane group 0 has a high chunk, d 64..79; the others hold zeros).
+template <int D, bool MX = false>
 __device__ __forceinline__ int k_lane_offset(int g, int i16, int lane) {
   if (Cfg<D>::KOP) return 16 * lane;
   const int krow = 4 * (i16 & 3) + (i16 >> 2);            // row of key 32*(i16/4) + i16%4
+  if (MX) return krow * Cfg<D>::KS + 16 * g;
   return krow * Cfg<D>::KS + (D == 72 ? min(32 * g, 64) : 32 * g);
 }
-template <int D>
-__device__ __forceinline__ v8i k_operand(const lds_u8* kl, int t) {
+// hi_keep: MX hd72 only, false where the lane group has no high chunk.
+template <int D, bool MX = false>
+__device__ __forceinline__ v8i k_operand(const lds_u8* kl, int t, bool hi_keep = true) {
   const lds_u8* kp = kl + (Cfg<D>::KOP ? 2048 * t : 16 * t * Cfg<D>::KS);
   const v4i k0 = *(const lds_v4i*)(kp);
+  if constexpr (MX && !Cfg<D>::KOP) {
+    static_assert(D == 72, "MX rows placement is the hd72 one");
+    // lane group 0 reads row bytes 64..79; the others read their low chunk
+    // again (in bounds) and drop it
+    const v4i k1 = *(const lds_v4i*)(kp + (hi_keep ? 64 : 0));
+    const v4i z = v4i{0, 0, 0, 0};
+    return __builtin_shufflevector(k0, hi_keep ? k1 : z, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
   const v4i k1 = *(const lds_v4i*)(kp + (Cfg<D>::KOP ? 1024 : 16));
   return __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7);
 }
@@ -254,7 +270,13 @@ __device__ __forceinline__ void dma_issue(__amdgpu_buffer_rsrc_t krs, __amdgpu_b
   }
 }
 
-template <int D, bool OUT8, bool WIDE>
+// MX: the block-scaled variant. Q and K carry one E8M0 scale per 32-element
+// block of head_dim (a.qs, a.ks: four bytes per (token, head)); the S^T MFMA
+// applies them per lane (lane group g supplies the scale of block g of its
+// row; the operands hold d in the MFMA's natural K order, see the K placement
+// above), so S comes out in true units and the softmax constant is
+// softmax_scale * log2(e). V keeps its per-tensor scale.
+template <int D, bool OUT8, bool WIDE, bool MX = false>
 __global__ __launch_bounds__((64 * Shape<D, WIDE>::WAVES))
 __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn_kernel(AttnArgs a) {
   using C = Cfg<D>;
@@ -269,6 +291,8 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
   // the DMA before each LDS read.
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[S::KBUF];
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[S::KBUF];
+  __shared__ __attribute__((aligned(256))) uint32_t ks_lds0[MX ? kBN : 1];   // K block scales of a tile, per key
+  __shared__ __attribute__((aligned(256))) uint32_t ks_lds1[MX ? kBN : 1];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[S::VBUF];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[S::VBUF];
   __shared__ __attribute__((aligned(1024))) uint8_t vh_lds0[SH::P16 ? S::VHBUF : 16];
@@ -315,7 +339,8 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
   for (int n = 0; n < S::NIW; ++n) {
     const int i = wave + SH::WAVES * n;
     if (i < S::NIK && C::KOP) {
-      dma_off[n] = (uint32_t)k_block_key(i >> 1, i16) * row_stride + 32u * g + 16u * (i & 1);
+      dma_off[n] = (uint32_t)k_block_key(i >> 1, i16) * row_stride +
+                   (MX ? 16u * g + 64u * (i & 1) : 32u * g + 16u * (i & 1));
     } else if (i < S::NIK) {
       const int c = 64 * i + lane;
       const int row = c / (C::KS / 16), piece = c % (C::KS / 16);
@@ -325,14 +350,29 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
       dma_off[n] = (uint32_t)(c / (C::VS / 16)) * row_stride + 16u * (uint32_t)(c % (C::VS / 16));
     }
   }
-  // Issue this wave's DMA of K tile tk into kdst and (with_v) V tile tv into vdst.
-  auto dma_tiles = [&](int tk, uint8_t* kdst, int tv, uint8_t* vdst, bool with_v) {
+  // MX: the K tile's scale dwords (four E8M0 bytes per key) come with it,
+  // 4 bytes per lane, waves 0 and 1 moving 64 keys each.
+  __amdgpu_buffer_rsrc_t ksrs;
+  if constexpr (MX) {
+    const uint32_t rows = a.tensor_bytes / D;   // T * H
+    const uint32_t first = (uint32_t)s0 * (uint32_t)a.H + (uint32_t)h;
+    ksrs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.ks + 4u * first), (short)0, (int)(4u * (rows - first)),
+                                             kRsrcWord3);
+  }
+  // Issue this wave's DMA of K tile tk into kdst (with its scales into ksdst,
+  // MX) and (with_v) V tile tv into vdst.
+  auto dma_tiles = [&](int tk, uint8_t* kdst, uint32_t* ksdst, int tv, uint8_t* vdst, bool with_v) {
     dma_issue<D, SH::WAVES>(krs, vrs, dma_off, wave, (uint32_t)tk * kBN * row_stride, kdst, (uint32_t)tv * kBN * row_stride,
                  vdst, with_v);
+    if constexpr (MX) {
+      if (wave < 2)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrs, (lds_void*)(ksdst + 64 * wave), 4,
+                                                 ((uint32_t)tk * kBN + 64u * wave + lane) * 4u * (uint32_t)a.H, 0, 0, 0);
+    }
   };
 
-  dma_tiles(0, k_lds0, 0, v_lds0, !SH::XT);    // K(0), and V(0) unless iteration 0 loads it
-  dma_tiles(1, k_lds1, 1, v_lds1, SH::P16);    // K(1), and V(1) for the widening pipeline
+  dma_tiles(0, k_lds0, ks_lds0, 0, v_lds0, !SH::XT);    // K(0), and V(0) unless iteration 0 loads it
+  dma_tiles(1, k_lds1, ks_lds1, 1, v_lds1, SH::P16);    // K(1), and V(1) for the widening pipeline
   if constexpr (!C::KOP) {
     // Zero the 32 bytes after each K tile (read only against zero Q bytes).
     for (int r = tid; r < 2 * 4; r += S::THREADS)
@@ -340,17 +380,38 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
   }
 
   const float dq = a.st->descale_used[0], dk = a.st->descale_used[1], dv = a.st->descale_used[2];
-  const float cexp = a.softmax_scale * dq * dk * kLog2e;   // raw score -> log2 units (> 0)
+  // raw score -> log2 units (> 0); MX scores already carry the block scales
+  const float cexp = MX ? a.softmax_scale * kLog2e : a.softmax_scale * dq * dk * kLog2e;
 
   // ---- Q operands (B of S^T): lane holds query i16 of its block, d bytes 32g.. ----
   v8i qop[QB];
+  int qsc[QB];   // MX: E8M0 scale of this lane's block g of its query (127 = 1.0 where no query)
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     qop[qb] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    qsc[qb] = 127;
     const int qr = q0 + wave * BMW + qb * 16 + i16;
     if (qr < L) {
+      if (MX) qsc[qb] = a.qs[((int64_t)(s0 + qr) * a.H + h) * 4 + g];
       const uint8_t* src = a.q8 + ((int64_t)(s0 + qr) * a.H + h) * D;
-      if (D == 72) {
+      if (MX && D == 72) {
+        // natural K order: d 16 g .. 16 g + 15, then (lane group 0) d 64..71
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          uint2 u = *reinterpret_cast<const uint2*>(src + 16 * g + 8 * j);
+          qop[qb][2 * j] = (int)u.x;
+          qop[qb][2 * j + 1] = (int)u.y;
+        }
+        if (g == 0) {
+          uint2 u = *reinterpret_cast<const uint2*>(src + 64);
+          qop[qb][4] = (int)u.x;
+          qop[qb][5] = (int)u.y;
+        }
+      } else if (MX) {
+        const v4i u0 = *reinterpret_cast<const v4i*>(src + 16 * g);
+        const v4i u1 = *reinterpret_cast<const v4i*>(src + 64 + 16 * g);
+        qop[qb] = __builtin_shufflevector(u0, u1, 0, 1, 2, 3, 4, 5, 6, 7);
+      } else if (D == 72) {
         if (g < 2) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -383,7 +444,8 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's DMA of K(0), K(1), V(0)
   __syncthreads();
-  const int kl_lane = k_lane_offset<D>(g, i16, lane);
+  const int kl_lane = k_lane_offset<D, MX>(g, i16, lane);
+  const bool k_hi = (D != 72) || (g == 0);   // MX hd72: lane groups with a high K chunk
   const int vl_lane = v_lane_offset<D>(g, i16);
   const int vhl_lane = 16 * lane;
   if constexpr (SH::P16) widen_v<D, SH::WAVES>(v_lds0, vh_lds0, wave, g, i16, vl_lane);   // V(0)
@@ -414,6 +476,22 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
     return r;
   };
 
+  // S^T block t of one query block: K rows as A, Q as B. MX: the lane's row of
+  // block t is key 32 (i16 / 4) + 4 t + i16 % 4; its scale byte g comes from
+  // the tile's scale dwords in LDS.
+  const int ks_key0 = 32 * (i16 >> 2) + (i16 & 3);
+  auto k_scale = [&](const uint32_t* ksbuf, int t) -> int {
+    if constexpr (MX) {
+      const uint32_t w = ((const __attribute__((address_space(3))) uint32_t*)ksbuf)[ks_key0 + 4 * t];
+      return (int)((w >> (8 * g)) & 0xffu);
+    }
+    return 0;
+  };
+  auto s_mfma = [&](const v8i& kop, int ksv, int qb) -> v4f {
+    if constexpr (MX) return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop, qop[qb], zero4, 0, 0, 0, ksv, 0, qsc[qb]);
+    return mfma_fp8(kop, qop[qb], zero4);
+  };
+
   // S(0)
   v4f sc[QB][8];
   {
@@ -422,9 +500,10 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
     const lds_u8* kl = (const lds_u8*)k_lds0 + kbase;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const v8i kop = k_operand<D>(kl, t);
+      const v8i kop = k_operand<D, MX>(kl, t, k_hi);
+      const int ksv = k_scale(ks_lds0, t);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sc[qb][t] = mfma_fp8(kop, qop[qb], zero4);
+      for (int qb = 0; qb < QB; ++qb) sc[qb][t] = s_mfma(kop, ksv, qb);
     }
   }
 
@@ -434,14 +513,16 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
     constexpr bool LAST = decltype(last_c)::value;
     constexpr bool ODD = decltype(odd_c)::value;
     uint8_t* const k_fill = ODD ? k_lds1 : k_lds0;         // K(j+2)
+    uint32_t* const ks_fill = ODD ? ks_lds1 : ks_lds0;
     uint8_t* const v_fill = ODD ? v_lds0 : v_lds1;         // V(j+1)
     const uint8_t* const k_read = ODD ? k_lds0 : k_lds1;   // K(j+1)
+    const uint32_t* const ks_read = ODD ? ks_lds0 : ks_lds1;
     const uint8_t* const v_read = ODD ? v_lds1 : v_lds0;   // V(j)
     // The previous iteration's reads of the buffers refilled below are done,
     // and this wave's DMA of K(j+1) and V(j) has landed, on every wave.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    dma_tiles(j + 2, k_fill, j + 1, v_fill, true);
+    dma_tiles(j + 2, k_fill, ks_fill, j + 1, v_fill, true);
     if (LAST) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
@@ -491,7 +572,7 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
     // P(j) block by block, each followed by the S(j+1) product of that block
     // (its K operand read one step ahead).
     v8i kop;
-    if (!LAST) kop = k_operand<D>(kl, 0);
+    if (!LAST) kop = k_operand<D, MX>(kl, 0, k_hi);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
 #pragma unroll
@@ -502,9 +583,10 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
       }
       if (!LAST) {
         const v8i kcur = kop;
-        if (t + 1 < 8) kop = k_operand<D>(kl, t + 1);
+        if (t + 1 < 8) kop = k_operand<D, MX>(kl, t + 1, k_hi);
+        const int ksv = k_scale(ks_read, t);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sc[qb][t] = mfma_fp8(kcur, qop[qb], zero4);
+        for (int qb = 0; qb < QB; ++qb) sc[qb][t] = s_mfma(kcur, ksv, qb);
       }
       // One query block per wave (4 waves/SIMD, 128 VGPRs): keep the steps
       // apart, since hoisting later LDS reads or softmax work into this step
@@ -542,14 +624,16 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
     constexpr bool LAST = decltype(last_c)::value;
     constexpr bool ODD = decltype(odd_c)::value;
     uint8_t* const k_fill = ODD ? k_lds1 : k_lds0;          // K(j+2)
+    uint32_t* const ks_fill = ODD ? ks_lds1 : ks_lds0;
     uint8_t* const v_fill = ODD ? v_lds1 : v_lds0;          // e4m3 V(j+2)
     const uint8_t* const v_conv = ODD ? v_lds0 : v_lds1;    // e4m3 V(j+1)
     uint8_t* const vh_fill = ODD ? vh_lds0 : vh_lds1;       // f16 V(j+1)
     const uint8_t* const k_read = ODD ? k_lds0 : k_lds1;    // K(j+1)
+    const uint32_t* const ks_read = ODD ? ks_lds0 : ks_lds1;
     const uint8_t* const vh_read = ODD ? vh_lds1 : vh_lds0; // f16 V(j)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    dma_tiles(j + 2, k_fill, j + 2, v_fill, true);
+    dma_tiles(j + 2, k_fill, ks_fill, j + 2, v_fill, true);
     if (!LAST) widen_v<D, SH::WAVES>(v_conv, vh_fill, wave, g, i16, vl_lane);
     if (LAST) {
 #pragma unroll
@@ -596,7 +680,7 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
     const lds_u8* kl = (const lds_u8*)k_read + kbase;
     const lds_u8* vhl = (const lds_u8*)vh_read + vbase;
     v8i kop;
-    if (!LAST) kop = k_operand<D>(kl, 0);
+    if (!LAST) kop = k_operand<D, MX>(kl, 0, k_hi);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
 #pragma unroll
@@ -610,9 +694,10 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
       }
       if (!LAST) {
         const v8i kcur = kop;
-        if (t + 1 < 8) kop = k_operand<D>(kl, t + 1);
+        if (t + 1 < 8) kop = k_operand<D, MX>(kl, t + 1, k_hi);
+        const int ksv = k_scale(ks_read, t);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sc[qb][t] = mfma_fp8(kcur, qop[qb], zero4);
+        for (int qb = 0; qb < QB; ++qb) sc[qb][t] = s_mfma(kcur, ksv, qb);
       }
       // O^T += V(j)^T P(j)^T for the 32-key chunk whose P is now complete,
       // so the P.V products spread over the softmax work of the tile.
@@ -653,12 +738,14 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
     constexpr bool LAST = decltype(last_c)::value;
     constexpr bool ODD = decltype(odd_c)::value;
     uint8_t* const k_fill = ODD ? k_lds1 : k_lds0;         // K(j+2)
+    uint32_t* const ks_fill = ODD ? ks_lds1 : ks_lds0;
     uint8_t* const v_fill = ODD ? v_lds1 : v_lds0;         // V(j)
     const uint8_t* const k_read = ODD ? k_lds0 : k_lds1;   // K(j+1)
+    const uint32_t* const ks_read = ODD ? ks_lds0 : ks_lds1;
     const uint8_t* const v_read = ODD ? v_lds0 : v_lds1;   // V(j-1)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    dma_tiles(j + 2, k_fill, j, v_fill, true);
+    dma_tiles(j + 2, k_fill, ks_fill, j, v_fill, true);
     if (LAST) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
@@ -704,7 +791,7 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
     const lds_u8* kl = (const lds_u8*)k_read + kbase;
     const lds_u8* vl = (const lds_u8*)v_read + vbase;
     v8i kop, vop;
-    if (!LAST) kop = k_operand<D>(kl, 0);
+    if (!LAST) kop = k_operand<D, MX>(kl, 0, k_hi);
     if (!FIRST) vop = v_op(vl, 0);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -726,9 +813,10 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
       }
       if (!LAST) {
         const v8i kcur = kop;
-        if (t + 1 < 8) kop = k_operand<D>(kl, t + 1);
+        if (t + 1 < 8) kop = k_operand<D, MX>(kl, t + 1, k_hi);
+        const int ksv = k_scale(ks_read, t);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sc[qb][t] = mfma_fp8(kcur, qop[qb], zero4);
+        for (int qb = 0; qb < QB; ++qb) sc[qb][t] = s_mfma(kcur, ksv, qb);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1329,7 +1417,7 @@ int64_t tiles_ub(int bm, int64_t total_tokens, int64_t nseg, int64_t max_seqlen)
   return by_total < by_max ? by_total : by_max;
 }
 
-template <int D, bool WIDE>
+template <int D, bool WIDE, bool MX = false>
 hipError_t launch_shape(AttnArgs a, int total_tokens, int max_seqlen, hipStream_t s) {
   a.ntiles_ub = (int32_t)tiles_ub(Shape<D, WIDE>::BM, total_tokens, a.nseg, max_seqlen);
   a.nsplit = 1;   // the key split exists in the wide hd72 kernel only
@@ -1338,9 +1426,9 @@ hipError_t launch_shape(AttnArgs a, int total_tokens, int max_seqlen, hipStream_
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 block(64 * Shape<D, WIDE>::WAVES);
   if (a.out8 != nullptr)
-    hipLaunchKernelGGL((attn_kernel<D, true, WIDE>), dim3((unsigned)grid), block, 0, s, a);
+    hipLaunchKernelGGL((attn_kernel<D, true, WIDE, MX>), dim3((unsigned)grid), block, 0, s, a);
   else
-    hipLaunchKernelGGL((attn_kernel<D, false, WIDE>), dim3((unsigned)grid), block, 0, s, a);
+    hipLaunchKernelGGL((attn_kernel<D, false, WIDE, MX>), dim3((unsigned)grid), block, 0, s, a);
   return hipGetLastError();
 }
 hipError_t launch_w32(AttnArgs a, int total_tokens, int max_seqlen, hipStream_t s) {
@@ -1419,6 +1507,15 @@ hipError_t launch_attn(const AttnArgs& a, int head_dim, int total_tokens, int ma
   static_assert(w32::BM == 256 && Shape<128, true>::BM == 256, "wide shapes");
   const int64_t wide_items = (int64_t)a.H * tiles_ub(256, total_tokens, a.nseg, max_seqlen);
   const bool wide = 2 * wide_items >= (int64_t)cus;
+  if (a.qs != nullptr) {
+    // Block-scaled Q and K: the kernels built on the scaled 16x16x128 MFMA
+    // (one scale per lane group and operand row); head_dim 72 runs the
+    // narrow shape.
+    if (head_dim == 128)
+      return wide ? launch_shape<128, true, true>(a, total_tokens, max_seqlen, s)
+                  : launch_shape<128, false, true>(a, total_tokens, max_seqlen, s);
+    return launch_shape<72, false, true>(a, total_tokens, max_seqlen, s);
+  }
   if (head_dim == 128)
     return wide ? launch_shape<128, true>(a, total_tokens, max_seqlen, s)
                 : launch_shape<128, false>(a, total_tokens, max_seqlen, s);

@@ -58,9 +58,13 @@ struct QuantArgs {
   int32_t T;
   int32_t row8;   // H*d/8 (16-byte chunks per token row)
   int32_t amax_blocks;  // workgroups of the amax pass (partial maxima to reduce)
+  uint32_t quant_mask;  // tensors the quantize pass writes (bit 0 q, 1 k, 2 v)
   DevState* st;
 };
 hipError_t launch_quantize(const QuantArgs& a, bool dynamic, hipStream_t s);
+// Block-scaled e4m3 codes [T, H, d] and E8M0 scales [T, H, 4] of one bf16 tensor.
+hipError_t launch_quantize_mx(const uint16_t* x, int64_t ld, int32_t T, int32_t H, int32_t d, uint8_t* codes,
+                              uint8_t* scales, hipStream_t s);
 
 struct AttnArgs {
   const uint8_t* q8;
@@ -77,6 +81,10 @@ struct AttnArgs {
   const float* out_descale;  // device fp32, with out8
   int64_t ld_out;          // token stride of the output, elements
   float softmax_scale;
+  // Block-scaled variant: E8M0 scales of Q and K, four bytes per (token,
+  // head); null for the per-tensor path.
+  const uint8_t* qs;
+  const uint8_t* ks;
   // Key split (the wide hd72 kernel): every (head, query tile) item's key
   // tiles are cut into up to nsplit pieces, one workgroup each; the pieces
   // leave normalised partial outputs in ws_slots, and a second kernel

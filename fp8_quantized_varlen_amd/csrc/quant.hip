@@ -114,7 +114,8 @@ template <bool CONTIG, bool NT>
 __device__ __forceinline__ void load3(const QuantArgs& a, uint32_t c, uint32_t n8, uint4 w[3]) {
 #pragma unroll
   for (int x = 0; x < 3; ++x)
-    w[x] = c < n8 ? ld16<NT>(chunk_src<CONTIG>(a.x[x], a.ld[x], a.row8, c)) : make_uint4(0, 0, 0, 0);
+    w[x] = (c < n8 && (a.quant_mask >> x & 1u)) ? ld16<NT>(chunk_src<CONTIG>(a.x[x], a.ld[x], a.row8, c))
+                                                : make_uint4(0, 0, 0, 0);
 }
 
 // Quantize this thread's chunks c = gtid + i * gstride of Q, K and V.
@@ -136,7 +137,8 @@ __device__ __forceinline__ void quantize_all(const QuantArgs& a, uint32_t n8, co
       load3<CONTIG, NT>(a, c, n8, cur);
     }
 #pragma unroll
-    for (int x = 0; x < 3; ++x) st8<NT>(reinterpret_cast<uint2*>(a.y[x]) + c, quant_chunk(cur[x], r[x]));
+    for (int x = 0; x < 3; ++x)
+      if (a.quant_mask >> x & 1u) st8<NT>(reinterpret_cast<uint2*>(a.y[x]) + c, quant_chunk(cur[x], r[x]));
   }
 }
 
@@ -248,6 +250,72 @@ __global__ __launch_bounds__(kQuantThreads) void amax_kernel(QuantArgs a) {
   absmax_all<CONTIG>(a, n8, gtid, gstride, m);
   block_max3(m, red);
   if (threadIdx.x == 0) *reinterpret_cast<uint4*>(st->amax_part[blockIdx.x]) = make_uint4(m[0], m[1], m[2], 0u);
+}
+
+// Block-scaled (MX) e4m3 quantization of one tensor (Q or K of the
+// block-scaled variant; FlashInfer PR 5283 analysis, Code analysis section 1:
+// a scale per block of the head dimension from the block's amax over the
+// element format's largest value). One thread per (token, head, 32-element
+// block of head_dim; a trailing partial block is its own block):
+//   s = the smallest integer with 448 * 2^s >= block amax (-127 for a zero or
+//       subnormal-only block; never above 120 for finite bf16 inputs),
+//   code_i = e4m3 RNE of clamp(x_i * 2^-s, +-448) (the product is exact),
+//   scale byte = s + 127 (E8M0), four bytes per (token, head), unused ones 0.
+// From the bf16 bits of the amax 2^E * (1 + m/128): 448 * 2^(E-8) = 1.75 * 2^E,
+// so s = E - 8 when m <= 96 (1 + m/128 <= 1.75) and E - 7 otherwise.
+__global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restrict__ x, int64_t ld, int32_t T,
+                                                       int32_t H, int32_t d, uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales) {
+  const int nb = (d + 31) / 32;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = tid / nb;
+  const int b = (int)(tid - row * nb);
+  if (row >= (int64_t)T * H) return;
+  const int64_t t = row / H, h = row - t * H;
+  const int n8 = min(32, d - 32 * b) / 8;   // 16-byte chunks in this block (4, or 1 for head_dim 72's last)
+  const uint4* src = reinterpret_cast<const uint4*>(x + t * ld + h * d + 32 * b);
+  uint4 w[4];
+  uint32_t m = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    w[c] = c < n8 ? src[c] : make_uint4(0, 0, 0, 0);
+    m = max(m, chunk_absmax_bits(w[c]));
+  }
+  const int efield = (int)(m >> 7), mant = (int)(m & 0x7f);
+  const int sexp = efield == 0 ? -127 : max(efield - 127 - 8 + (mant > 96 ? 1 : 0), -127);
+  const float r = __uint_as_float((uint32_t)(127 - sexp) << 23);   // 2^-s, a normal float for s in [-127, 120]
+  uint8_t* dst = codes + row * d + 32 * b;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (c < n8) {
+      uint32_t wv[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
+      uint32_t out[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const float y0 = __builtin_amdgcn_fmed3f(__uint_as_float(bf16_lo(wv[2 * hh])) * r, -kFp8Max, kFp8Max);
+        const float y1 = __builtin_amdgcn_fmed3f(__uint_as_float(bf16_hi(wv[2 * hh])) * r, -kFp8Max, kFp8Max);
+        const float y2 = __builtin_amdgcn_fmed3f(__uint_as_float(bf16_lo(wv[2 * hh + 1])) * r, -kFp8Max, kFp8Max);
+        const float y3 = __builtin_amdgcn_fmed3f(__uint_as_float(bf16_hi(wv[2 * hh + 1])) * r, -kFp8Max, kFp8Max);
+        int p = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+        out[hh] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, p, true);
+      }
+      *reinterpret_cast<uint2*>(dst + 8 * c) = make_uint2(out[0], out[1]);
+    }
+  }
+  uint8_t* sp = scales + row * 4;
+  sp[b] = (uint8_t)(sexp + 127);
+  if (b == nb - 1)
+    for (int pb = nb; pb < 4; ++pb) sp[pb] = 0;
+}
+
+hipError_t launch_quantize_mx(const uint16_t* x, int64_t ld, int32_t T, int32_t H, int32_t d, uint8_t* codes,
+                              uint8_t* scales, hipStream_t s) {
+  const int64_t threads = (int64_t)T * H * ((d + 31) / 32);
+  if (threads == 0) return hipSuccess;
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(mx_quant_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, ld, T, H, d, codes, scales);
+  return hipGetLastError();
 }
 
 hipError_t launch_quantize(const QuantArgs& a, bool dynamic, hipStream_t s) {

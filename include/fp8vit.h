@@ -252,6 +252,53 @@ fp8vit_status fp8vit_attn_varlen_noalloc(const void* q8, const void* k8, const v
                                          int32_t head_dim, float softmax_scale, const void* d_state,
                                          void* out, int64_t ld_out, void* stream);
 
+/* Block-scaled ("MX") variant of fp8vit_quantize_qkv: Q and K get one
+ * power-of-two scale per 32-element block of head_dim instead of one per
+ * tensor; V is quantized exactly as by fp8vit_quantize_qkv (per-tensor scale
+ * from `mode`; in dynamic mode the amax ring of Q, K and V is kept as there).
+ *   q8, k8        e4m3 codes [T, H, d] (16-byte aligned): code of
+ *                 clamp(x / 2^s_b, +-448), nearest-even, where s_b is the
+ *                 block's scale exponent (the product x * 2^-s_b is exact).
+ *   q_scales,
+ *   k_scales      uint8 [T, H, 4] (4-byte aligned): byte b is the E8M0 scale
+ *                 (s_b + 127) of block b = elements 32b .. min(d, 32b + 32);
+ *                 head_dim 72 has three blocks (the third of 8 elements) and
+ *                 byte 3 = 0; head_dim 128 has four.
+ *   s_b          the smallest integer with 448 * 2^s_b >= the block's amax
+ *                 (so no element saturates), -127 for a block of zeros.
+ * v8, state, mode, strides, alignment and errors as fp8vit_quantize_qkv, and
+ * ERR_UNSUPPORTED for head_dim other than 72 or 128. Up to four launches
+ * (dynamic amax pass, V, Q, K).
+ * Source: FlashInfer PR 5283 analysis ("experimental NVFP4 attention"), Code
+ * analysis section 1 (a scale per block of the head dimension from the block
+ * amax over the element format's largest value); PR 3684 analysis
+ * ("asymmetric VO-split NVFP4"), section 3 (one scale factor per block). */
+fp8vit_status fp8vit_quantize_qkv_mx(const void* q, const void* k, const void* v,
+                                     int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                                     int32_t total_tokens, int32_t num_heads, int32_t head_dim,
+                                     int32_t mode, void* q8, void* k8, void* v8, void* q_scales,
+                                     void* k_scales, void* d_state, void* stream);
+
+/* fp8vit_attn_varlen for block-scaled Q and K (as written by
+ * fp8vit_quantize_qkv_mx): S = Q^ K^T with each 32-element block of Q and K
+ * dequantized by its own power-of-two scale, applied by the gfx950 matrix
+ * core (v_mfma_scale_f32_16x16x128_f8f6f4, which takes one E8M0 byte per
+ * operand row and 32-element block); V uses the per-tensor descale in d_state.
+ * Runs the 16x16 kernel family (head_dim 72: the narrow shape, whose P.V is
+ * two e4m3 terms on the FP8 MFMA; head_dim 128: narrow or wide). Arguments,
+ * layout and errors as fp8vit_attn_varlen, with d_q_scales and d_k_scales
+ * the [T, H, 4] scale bytes (device, 4-byte aligned, non-null unless the
+ * problem is empty).
+ * Source: FlashInfer PR 5283 analysis, Code analysis section 1 (attention on
+ * block-scaled Q and K); vLLM page "FP8 ViT Encoder Attention", Requirements
+ * (varlen FP8 attention). */
+fp8vit_status fp8vit_attn_varlen_mx(const void* q8, const void* k8, const void* v8,
+                                    const void* d_q_scales, const void* d_k_scales,
+                                    const int32_t* d_cu_seqlens, int32_t num_segments,
+                                    int32_t max_seqlen, int32_t total_tokens, int32_t num_heads,
+                                    int32_t head_dim, float softmax_scale, const void* d_state,
+                                    void* out, int64_t ld_out, void* stream);
+
 /* fp8vit_attn_varlen with an e4m3 output, to feed an FP8 output projection
  * without a separate quantization pass (the fused fp8-output request on the
  * vLLM issue page "Add support for fused fp8 output to FlashAttention 3").
