@@ -196,19 +196,17 @@ def attn_kernel_name(w, dev, out8, mx=False):
     """Name of the attention kernel instance the library launches for this
     workload, as the profiler prints it: the wide shape (256 queries per
     workgroup) is used once its workgroups cover at least half of the CUs; at
-    head dim 72 it is the 32x32-block kernel attn_w32_kernel, except with
-    block-scaled Q and K (mx), which run the narrow hd72 shape."""
+    head dim 72 it is the 32x32-block kernel attn_w32_kernel."""
     import torch
     d = w.head_dim
     T, nseg, L = w.total_tokens, len(w.seglens), max(w.seglens)
     tiles = min((T + 255) // 256 + nseg, nseg * ((L + 255) // 256))
     wide = 2 * w.heads * tiles >= torch.cuda.get_device_properties(dev).multi_processor_count
     o8 = "true" if out8 else "false"
-    if mx:
-        return "attn_kernel<%d, false, %s, true>" % (d, "true" if wide and d == 128 else "false")
+    m = "true" if mx else "false"
     if wide and d == 72:
-        return "attn_w32_kernel<%s>" % o8
-    return "attn_kernel<%d, %s, %s, false>" % (d, o8, "true" if wide else "false")
+        return "attn_w32_kernel<%s, %s>" % (o8, m)
+    return "attn_kernel<%d, %s, %s, %s>" % (d, o8, "true" if wide else "false", m)
 
 
 def attn_traffic(workload, head_dim):

@@ -1119,13 +1119,15 @@ __global__ __launch_bounds__(2 * kSplitQueries) void attn_split_combine_kernel(A
   }
 }
 
-template <bool OUT8>
+template <bool OUT8, bool MX = false>
 __global__ __launch_bounds__(64 * w32::WAVES) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_w32_kernel(AttnArgs a) {
   using namespace w32;
   constexpr int D = 72;
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[KBUF];
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[KBUF];
+  __shared__ __attribute__((aligned(256))) uint32_t ks_lds0[MX ? kBN : 1];   // MX: K block scales, per key
+  __shared__ __attribute__((aligned(256))) uint32_t ks_lds1[MX ? kBN : 1];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[VBUF];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[VBUF];
   __shared__ __attribute__((aligned(1024))) uint8_t vh_lds0[VHBUF];
@@ -1174,7 +1176,8 @@ void attn_w32_kernel(AttnArgs a) {
       const int c = 64 * i + lane, u = c / 160, r = c % 160;
       if (r < 128) {
         const int hh = r >> 6, ln = r & 63;
-        dma_off[n] = (uint32_t)(32 * u + (ln & 31)) * row_stride + 32u * (uint32_t)(ln >> 5) + 16u * hh;
+        dma_off[n] = (uint32_t)(32 * u + (ln & 31)) * row_stride +
+                     (MX ? 16u * (uint32_t)(ln >> 5) + 32u * hh : 32u * (uint32_t)(ln >> 5) + 16u * hh);
       } else {
         dma_off[n] = (uint32_t)(32 * u + (r - 128)) * row_stride + 64u;
       }
@@ -1183,12 +1186,26 @@ void attn_w32_kernel(AttnArgs a) {
       dma_off[n] = (uint32_t)(c / 5) * row_stride + 16u * (uint32_t)(c % 5);
     }
   }
-  auto dma_tiles = [&](int tk, uint8_t* kdst, int tv, uint8_t* vdst, bool with_v) {
+  // MX: the K tile's scale dwords (four E8M0 bytes per key), 4 bytes per
+  // lane, waves 0 and 1 moving 64 keys each.
+  __amdgpu_buffer_rsrc_t ksrs;
+  if constexpr (MX) {
+    const uint32_t rows = a.tensor_bytes / D;   // T * H
+    const uint32_t first = (uint32_t)s0 * (uint32_t)a.H + (uint32_t)h;
+    ksrs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.ks + 4u * first), (short)0, (int)(4u * (rows - first)),
+                                             kRsrcWord3);
+  }
+  auto dma_tiles = [&](int tk, uint8_t* kdst, uint32_t* ksdst, int tv, uint8_t* vdst, bool with_v) {
     dma_issue<D, WAVES>(krs, vrs, dma_off, wave, (uint32_t)tk * kBN * row_stride, kdst,
                         (uint32_t)tv * kBN * row_stride, vdst, with_v);
+    if constexpr (MX) {
+      if (wave < 2)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrs, (lds_void*)(ksdst + 64 * wave), 4,
+                                                 ((uint32_t)tk * kBN + 64u * wave + lane) * 4u * (uint32_t)a.H, 0, 0, 0);
+    }
   };
-  dma_tiles(ja, k_lds0, ja, v_lds0, true);
-  dma_tiles(ja + 1, k_lds1, ja + 1, v_lds1, true);
+  dma_tiles(ja, k_lds0, ks_lds0, ja, v_lds0, true);
+  dma_tiles(ja + 1, k_lds1, ks_lds1, ja + 1, v_lds1, true);
   // Rows 80..95 of the widened V^T (no V columns) stay zero: in each buffer,
   // chunks 16..23 (block db = 2), lanes with l % 32 >= 16.
   for (int r = tid; r < 2 * 256; r += 64 * WAVES) {
@@ -1198,24 +1215,36 @@ void attn_w32_kernel(AttnArgs a) {
   }
 
   const float dq = a.st->descale_used[0], dk = a.st->descale_used[1], dv = a.st->descale_used[2];
-  const float cexp = a.softmax_scale * dq * dk * kLog2e;
+  // raw score -> log2 units; MX scores already carry the block scales
+  const float cexp = MX ? a.softmax_scale * kLog2e : a.softmax_scale * dq * dk * kLog2e;
 
-  // ---- Q operands: lane l: query l%32, d bytes 32 hf .. + 31, and 64 + 8 hf .. + 7 ----
+  // ---- Q operands: lane l: query l%32, d bytes 32 hf .. + 31 (MX: 16 hf .. + 15
+  // and 32 + 16 hf .. + 15), and 64 + 8 hf .. + 7 (MX: 64 .. 71 in lane half 0) ----
   v8i qa = v8i{0, 0, 0, 0, 0, 0, 0, 0};
   long qbv = 0;
+  int qs01 = 127, qs2 = 127;   // MX: E8M0 scales of the query's block hf and block 2
   {
     const int qr = q0 + wave * 32 + l32;
     if (qr < L) {
       const uint8_t* src = a.q8 + ((int64_t)(s0 + qr) * a.H + h) * D;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint2 u2 = *reinterpret_cast<const uint2*>(src + 32 * hf + 8 * j);
+        const uint2 u2 = *reinterpret_cast<const uint2*>(src + (MX ? 16 * hf + 32 * (j >> 1) + 8 * (j & 1)
+                                                                   : 32 * hf + 8 * j));
         qa[2 * j] = (int)u2.x;
         qa[2 * j + 1] = (int)u2.y;
       }
       if (hf == 0) qbv = *reinterpret_cast<const long*>(src + 64);
+      if (MX) {
+        const uint8_t* qsp = a.qs + ((int64_t)(s0 + qr) * a.H + h) * 4;
+        qs01 = qsp[hf];
+        qs2 = qsp[2];
+      }
     }
   }
+  // MX: d 64..71 go through a second scaled 32x32x64 product (block 2 in
+  // positions 0..7 of lane half 0, everything else zero).
+  const v8i qb8 = v8i{(int)qbv, (int)(qbv >> 32), 0, 0, 0, 0, 0, 0};
 
   v16f o[3];
 #pragma unroll
@@ -1232,23 +1261,38 @@ void attn_w32_kernel(AttnArgs a) {
   const int vl_lane = v_lane_offset<D>(g, i16);
   widen(v_lds0, vh_lds0, wave, g, i16, vl_lane);      // V(ja)
 
-  const int ka_lane = 16 * lane, kb_lane = 2048 + 16 * l32 + 8 * hf;
+  const int ka_lane = 16 * lane, kb_lane = 2048 + 16 * l32 + (MX ? 0 : 8 * hf);   // MX: d 64..71 in both halves
   auto k_a = [&](const lds_u8* kb, int u) -> v8i {
     const v4i x0 = *(const lds_v4i*)(kb + u * 2560 + ka_lane);
     const v4i x1 = *(const lds_v4i*)(kb + u * 2560 + ka_lane + 1024);
     return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
   };
   auto k_b = [&](const lds_u8* kb, int u) -> long { return *(const lds_i64*)(kb + u * 2560 + kb_lane); };
+  // S^T block u of the wave's queries from K buffer kb (MX: with the scale
+  // dwords ksb; lane l's row is key 32u + l%32).
+  auto s_block = [&](const lds_u8* kb, const uint32_t* ksb, int u) -> v16f {
+    if constexpr (MX) {
+      // The second product's A operand is the first one's with dwords 0..1
+      // replaced by d 64..71: the other dwords (finite codes) meet zero Q
+      // dwords, and so does lane half 1 (its Q dwords 0..1 are zero too).
+      const uint32_t ksw = ((const __attribute__((address_space(3))) uint32_t*)ksb)[32 * u + l32];
+      const v8i ka = k_a(kb, u);
+      const long kbv = k_b(kb, u);
+      const v16f s01 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          ka, qa, zero16, 0, 0, 0, (int)((ksw >> (8 * hf)) & 0xffu), 0, qs01);
+      const v8i kb8 = v8i{(int)kbv, (int)(kbv >> 32), ka[2], ka[3], ka[4], ka[5], ka[6], ka[7]};
+      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kb8, qb8, s01, 0, 0, 0, (int)((ksw >> 16) & 0xffu), 0,
+                                                             qs2);
+    }
+    return mfma16(k_b(kb, u), qbv, mfma64(k_a(kb, u), qa, zero16));
+  };
 
   // S(ja)
   v16f sc[4];
   {
     const lds_u8* kb = (const lds_u8*)k_lds0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      sc[u] = mfma64(k_a(kb, u), qa, zero16);
-      sc[u] = mfma16(k_b(kb, u), qbv, sc[u]);
-    }
+    for (int u = 0; u < 4; ++u) sc[u] = s_block(kb, ks_lds0, u);
   }
 
   int pf[4][8];   // f16 P~ of block u: dwords 4qq .. 4qq+3 are chunk (u, qq)
@@ -1256,14 +1300,16 @@ void attn_w32_kernel(AttnArgs a) {
     constexpr bool LAST = decltype(last_c)::value;
     constexpr bool ODD = decltype(odd_c)::value;
     uint8_t* const k_fill = ODD ? k_lds1 : k_lds0;          // K(j+2)
+    uint32_t* const ks_fill = ODD ? ks_lds1 : ks_lds0;      // its scales (MX)
     uint8_t* const v_fill = ODD ? v_lds1 : v_lds0;          // e4m3 V(j+2)
     const uint8_t* const v_conv = ODD ? v_lds0 : v_lds1;    // e4m3 V(j+1)
     uint8_t* const vh_fill = ODD ? vh_lds0 : vh_lds1;       // f16 V(j+1)
     const uint8_t* const k_read = ODD ? k_lds0 : k_lds1;    // K(j+1)
+    const uint32_t* const ks_read = ODD ? ks_lds0 : ks_lds1;
     const uint8_t* const vh_read = ODD ? vh_lds1 : vh_lds0; // f16 V(j)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    dma_tiles(j + 2, k_fill, j + 2, v_fill, true);
+    dma_tiles(j + 2, k_fill, ks_fill, j + 2, v_fill, true);
     if (!LAST) widen(v_conv, vh_fill, wave, g, i16, vl_lane);
     if (LAST) {
 #pragma unroll
@@ -1306,10 +1352,7 @@ void attn_w32_kernel(AttnArgs a) {
         const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[u][r + 1], cexp, nb));
         pf[u][r >> 1] = __builtin_bit_cast(int, (v2h){(_Float16)p0, (_Float16)p1});
       }
-      if (!LAST) {
-        sc[u] = mfma64(k_a(kb, u), qa, zero16);
-        sc[u] = mfma16(k_b(kb, u), qbv, sc[u]);
-      }
+      if (!LAST) sc[u] = s_block(kb, ks_read, u);
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) {
         const v8h pb = __builtin_bit_cast(v8h, v4i{pf[u][4 * qq], pf[u][4 * qq + 1], pf[u][4 * qq + 2], pf[u][4 * qq + 3]});
@@ -1425,10 +1468,15 @@ hipError_t launch_shape(AttnArgs a, int total_tokens, int max_seqlen, hipStream_
   const int64_t grid = ((items + 7) / 8) * 8;
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 block(64 * Shape<D, WIDE>::WAVES);
-  if (a.out8 != nullptr)
-    hipLaunchKernelGGL((attn_kernel<D, true, WIDE, MX>), dim3((unsigned)grid), block, 0, s, a);
-  else
-    hipLaunchKernelGGL((attn_kernel<D, false, WIDE, MX>), dim3((unsigned)grid), block, 0, s, a);
+  if constexpr (MX) {
+    // block-scaled Q and K: bf16 output only
+    if (a.out8 != nullptr) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_kernel<D, false, WIDE, true>), dim3((unsigned)grid), block, 0, s, a);
+  } else if (a.out8 != nullptr) {
+    hipLaunchKernelGGL((attn_kernel<D, true, WIDE>), dim3((unsigned)grid), block, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((attn_kernel<D, false, WIDE>), dim3((unsigned)grid), block, 0, s, a);
+  }
   return hipGetLastError();
 }
 hipError_t launch_w32(AttnArgs a, int total_tokens, int max_seqlen, hipStream_t s) {
@@ -1438,10 +1486,15 @@ hipError_t launch_w32(AttnArgs a, int total_tokens, int max_seqlen, hipStream_t 
   const int64_t grid = ((items + 7) / 8) * 8;
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 block(64 * w32::WAVES);
-  if (a.out8 != nullptr)
-    hipLaunchKernelGGL(attn_w32_kernel<true>, dim3((unsigned)grid), block, 0, s, a);
-  else
-    hipLaunchKernelGGL(attn_w32_kernel<false>, dim3((unsigned)grid), block, 0, s, a);
+  if (a.qs != nullptr) {
+    // block-scaled Q and K: bf16 output only
+    if (a.out8 != nullptr) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_w32_kernel<false, true>), dim3((unsigned)grid), block, 0, s, a);
+  } else if (a.out8 != nullptr) {
+    hipLaunchKernelGGL((attn_w32_kernel<true>), dim3((unsigned)grid), block, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((attn_w32_kernel<false>), dim3((unsigned)grid), block, 0, s, a);
+  }
   if (a.nsplit == 1) return hipGetLastError();
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1508,13 +1561,12 @@ hipError_t launch_attn(const AttnArgs& a, int head_dim, int total_tokens, int ma
   const int64_t wide_items = (int64_t)a.H * tiles_ub(256, total_tokens, a.nseg, max_seqlen);
   const bool wide = 2 * wide_items >= (int64_t)cus;
   if (a.qs != nullptr) {
-    // Block-scaled Q and K: the kernels built on the scaled 16x16x128 MFMA
-    // (one scale per lane group and operand row); head_dim 72 runs the
-    // narrow shape.
+    // Block-scaled Q and K: the same shapes with the block scales fed to the
+    // scaled MFMAs (one E8M0 byte per operand row and 32-element block).
     if (head_dim == 128)
       return wide ? launch_shape<128, true, true>(a, total_tokens, max_seqlen, s)
                   : launch_shape<128, false, true>(a, total_tokens, max_seqlen, s);
-    return launch_shape<72, false, true>(a, total_tokens, max_seqlen, s);
+    return wide ? launch_w32(a, total_tokens, max_seqlen, s) : launch_shape<72, false, true>(a, total_tokens, max_seqlen, s);
   }
   if (head_dim == 128)
     return wide ? launch_shape<128, true>(a, total_tokens, max_seqlen, s)

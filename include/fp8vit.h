@@ -284,9 +284,10 @@ fp8vit_status fp8vit_quantize_qkv_mx(const void* q, const void* k, const void* v
  * dequantized by its own power-of-two scale, applied by the gfx950 matrix
  * core (v_mfma_scale_f32_16x16x128_f8f6f4, which takes one E8M0 byte per
  * operand row and 32-element block); V uses the per-tensor descale in d_state.
- * Runs the 16x16 kernel family (head_dim 72: the narrow shape, whose P.V is
- * two e4m3 terms on the FP8 MFMA; head_dim 128: narrow or wide). Arguments,
- * layout and errors as fp8vit_attn_varlen, with d_q_scales and d_k_scales
+ * Runs the kernel shapes fp8vit_attn_varlen chooses, with no key split
+ * (head_dim 72 wide: v_mfma_scale_f32_32x32x64_f8f6f4 for d 0..63 and again
+ * for d 64..71). bf16 output only. Arguments, layout and errors as
+ * fp8vit_attn_varlen, with d_q_scales and d_k_scales
  * the [T, H, 4] scale bytes (device, 4-byte aligned, non-null unless the
  * problem is empty).
  * Source: FlashInfer PR 5283 analysis, Code analysis section 1 (attention on

@@ -71,8 +71,10 @@ def test_mx_quantize_strided_views():
     assert np.array_equal(codes_np(k8), rc) and np.array_equal(codes_np(ks), rs)
 
 
-# (segment lengths, heads, head_dim): narrow hd72, narrow hd128, wide hd128 (64 heads)
-MX_CASES = [((130, 1, 0, 257, 64), 3, 72), ((300, 129, 1), 2, 128), ((300, 129), 64, 128), ((700,), 16, 72)]
+# (segment lengths, heads, head_dim): narrow hd72, narrow hd128, wide hd128 (64 heads),
+# wide hd72 (attn_w32_kernel: 64 heads)
+MX_CASES = [((130, 1, 0, 257, 64), 3, 72), ((300, 129, 1), 2, 128), ((300, 129), 64, 128), ((700,), 16, 72),
+            ((300, 129, 0, 513), 64, 72)]
 
 
 @pytest.mark.parametrize("seglens,H,d", MX_CASES)
@@ -125,7 +127,7 @@ def test_mx_attention_block_scales_matter():
     assert err <= ATOL_FRAC_OF_VMAX, err
 
 
-@pytest.mark.parametrize("H,d", [(2, 72), (2, 128), (64, 128)])
+@pytest.mark.parametrize("H,d", [(2, 72), (2, 128), (64, 128), (64, 72)])
 def test_mx_attention_random_block_scales(H, d):
     """Scale bytes drawn independently per (token, head, block) for Q and K
     (2^-8 .. 2^-4) over the quantizer's codes: the attention must match the
@@ -154,3 +156,60 @@ def test_mx_attention_random_block_scales(H, d):
                                      oracle.mx.dequantize(codes_np(k8), scales[1]), vdeq, cu)
     err = np.abs(o.float().cpu().numpy() - ref).max() / np.abs(vdeq).max()
     assert err <= ATOL_FRAC_OF_VMAX, err
+
+
+@pytest.mark.parametrize("name", ["l8192_hd72_static", "l8192_hd128_dyn"])
+def test_mx_full_size_sampled(name):
+    """The block-scaled path at full size in the launch configuration of
+    `bench.py --scaling mx` (static values calibrated over the workload's 16
+    calibration inputs, or the ring filled by its 16 warm-ups): codes and
+    scales bit for bit, V's descale, and 2048 sampled rows plus the first and
+    last row of every head against the MX oracle and unquantized fp64."""
+    from synth import WORKLOADS
+    dev = require_gpu()
+    w = WORKLOADS[name]
+    st = fv.new_state(dev)
+    ring = oracle.scales.AmaxRing()
+    static_values = None
+    if w.mode == "static":
+        cal = fv.new_state(dev)
+        cal_ring = oracle.scales.AmaxRing()
+        for s in w.warm_seeds:
+            x = w.inputs(s)
+            fv.quantize_qkv(*(to_dev(t, dev) for t in x), cal, "dynamic")
+            cal_ring.push([oracle.quant.amax(t) for t in x])
+        static_values = fv.calibrated_values(cal, 1.5)
+        assert np.array_equal(np.float32(static_values), oracle.scales.calibrated_values(cal_ring, 1.5))
+        fv.state_set_static(st, static_values)
+    else:
+        for s in w.warm_seeds:
+            x = w.inputs(s)
+            fv.quantize_qkv(*(to_dev(t, dev) for t in x), st, "dynamic")
+            ring.push([oracle.quant.amax(t) for t in x])
+    qb, kb, vb = w.inputs()
+    q8, k8, v8, qs, ks = fv.quantize_qkv_mx(to_dev(qb, dev), to_dev(kb, dev), to_dev(vb, dev), st, w.mode)
+    T, H, d = qb.shape
+    L = max(w.seglens)
+    cu_d = torch.from_numpy(np.asarray(w.cu_seqlens, np.int32)).to(dev)
+    out = torch.full((T, H, d), float("nan"), dtype=torch.bfloat16, device=dev)
+    fv.attn_varlen_mx(q8, k8, v8, qs, ks, cu_d, L, st, out=out)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64)
+    assert not np.any(np.isnan(o)), "unwritten output elements"
+    ref = oracle.pipeline.forward_mx(qb, kb, vb, w.cu_seqlens, w.mode, ring=ring, static_values=static_values,
+                                     attend=False)
+    assert np.array_equal(codes_np(q8), ref.q[0]) and np.array_equal(codes_np(qs), ref.q[1])
+    assert np.array_equal(codes_np(k8), ref.k[0]) and np.array_equal(codes_np(ks), ref.k[1])
+    assert np.array_equal(codes_np(v8), ref.v_codes)
+    assert np.float32(fv.state_read(st)["descale_used"][2]) == ref.v_descale
+    rng = np.random.default_rng(11)
+    rows = list(zip(rng.integers(0, T, 2048).tolist(), rng.integers(0, H, 2048).tolist()))
+    rows += [(0, h) for h in range(H)] + [(T - 1, h) for h in range(H)]
+    deq = [oracle.mx.dequantize(*ref.q), oracle.mx.dequantize(*ref.k), oracle.quant.dequantize(ref.v_codes, ref.v_descale)]
+    want = oracle.attention.attention_rows(deq[0], deq[1], deq[2], w.cu_seqlens, rows)
+    got = np.stack([o[t, h] for t, h in rows])
+    err = np.abs(got - want).max() / vmax_of(vb)
+    assert err <= ATOL_FRAC_OF_VMAX, err
+    fp = [oracle.quant.bf16_to_f32(x) for x in (qb, kb, vb)]
+    unq = oracle.attention.attention_rows(fp[0], fp[1], fp[2], w.cu_seqlens, rows)
+    assert rel_rms(got, unq) <= REL_RMS_VS_FP64
