@@ -84,8 +84,12 @@ def _lib_handle():
 
 
 class _Lazy:
+    # First access to a name loads the library and keeps the function as an
+    # attribute, so later calls skip this method.
     def __getattr__(self, name):
-        return getattr(_lib_handle(), name)
+        fn = getattr(_lib_handle(), name)
+        setattr(self, name, fn)
+        return fn
 
 
 _lib = _Lazy()
@@ -108,7 +112,13 @@ def _check(fn: str, status: int) -> None:
         raise Fp8VitError(fn, status)
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(device: torch.device) -> int:
+    """The current stream of `device` as a raw hipStream_t."""
+    if _raw_stream is not None and device.index is not None:
+        return _raw_stream(device.index)
     return torch.cuda.current_stream(device).cuda_stream
 
 
@@ -116,8 +126,14 @@ def _ptr(t: Optional[torch.Tensor]) -> int:
     return 0 if t is None else t.data_ptr()
 
 
+_STATE_BYTES = None
+
+
 def state_bytes() -> int:
-    return int(_lib.fp8vit_state_bytes())
+    global _STATE_BYTES
+    if _STATE_BYTES is None:
+        _STATE_BYTES = int(_lib.fp8vit_state_bytes())
+    return _STATE_BYTES
 
 
 def state_init(state: torch.Tensor) -> torch.Tensor:
@@ -163,21 +179,26 @@ def _tensor(name: str, t) -> torch.Tensor:
 def _bhd(name: str, t, dtypes, shape=None, contiguous=False) -> torch.Tensor:
     """A [T, H, d] tensor with heads and head_dim contiguous (token stride free
     unless `contiguous`)."""
-    t = _tensor(name, t)
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
     if t.dtype not in dtypes:
         raise ValueError(f"{name} must have dtype {' or '.join(str(x) for x in dtypes)}, got {t.dtype}")
-    if t.dim() != 3:
-        raise ValueError(f"{name} must be 3-D [tokens, heads, head_dim], got shape {tuple(t.shape)}")
-    if shape is not None and tuple(t.shape) != tuple(shape):
-        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
-    T, H, d = t.shape
+    sh = t.shape
+    if len(sh) != 3:
+        raise ValueError(f"{name} must be 3-D [tokens, heads, head_dim], got shape {tuple(sh)}")
+    if shape is not None and sh != shape:
+        raise ValueError(f"{name} has shape {tuple(sh)}, expected {tuple(shape)}")
+    T, H, d = sh
     if T > 0 and H > 0 and d > 0:
-        if (H > 1 and t.stride(1) != d) or (d > 1 and t.stride(2) != 1):
+        s0, s1, s2 = t.stride()
+        if (H > 1 and s1 != d) or (d > 1 and s2 != 1):
             raise ValueError(f"{name}: heads and head_dim must be contiguous (strides {t.stride()})")
-        if contiguous and not t.is_contiguous():
+        # with heads and head_dim contiguous, [T, H, d] is contiguous iff the
+        # token stride is H*d (or there is one token)
+        if contiguous and T > 1 and s0 != H * d:
             raise ValueError(f"{name} must be contiguous [T, H, d]")
-        if t.stride(0) < H * d:
-            raise ValueError(f"{name}: token stride {t.stride(0)} is below H*d = {H * d}")
+        if s0 < H * d:
+            raise ValueError(f"{name}: token stride {s0} is below H*d = {H * d}")
     return t
 
 
@@ -191,10 +212,15 @@ def _state_tensor(state) -> torch.Tensor:
 
 def _same_gpu(**tensors) -> torch.device:
     """All tensors on one device, and that device a GPU."""
-    devs = {name: t.device for name, t in tensors.items() if t is not None}
-    first = next(iter(devs.values()))
-    if any(d != first for d in devs.values()):
-        raise ValueError("tensors are on different devices: " + ", ".join(f"{n}={d}" for n, d in devs.items()))
+    first = None
+    for t in tensors.values():
+        if t is None:
+            continue
+        if first is None:
+            first = t.device
+        elif t.device != first:
+            raise ValueError("tensors are on different devices: " +
+                             ", ".join(f"{n}={t.device}" for n, t in tensors.items() if t is not None))
     if first.type != "cuda":
         raise ValueError(f"tensors must be on a GPU, got {first}")
     return first
