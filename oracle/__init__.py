@@ -27,4 +27,4 @@ brute force, library routines, closed forms or invariants; the attention
 values themselves are never printed on the pages ("parity unpinned" against
 page values: pinned instead by brute force and invariants).
 """
-from . import e4m3, scales, quant, attention, mx, pipeline  # noqa: F401
+from . import e4m3, scales, quant, attention, mx, pipeline, varlen  # noqa: F401

@@ -55,3 +55,19 @@ def quantize(bits: np.ndarray, descale) -> np.ndarray:
 def dequantize(codes: np.ndarray, descale) -> np.ndarray:
     """Exact fp64 value of each code times the descale (3-bit x 24-bit fits in 53)."""
     return e4m3.decode(codes) * np.float64(np.float32(descale))
+
+
+def saturated_count(bits: np.ndarray, descale) -> int:
+    """Number of elements the clamp of the quantizer changes: those whose fp32
+    quotient x / descale (IEEE division) is larger than 448 in magnitude.
+
+    A diagnostic of static scales (vLLM page "FP8 ViT Encoder Attention",
+    Calibrate-Once Reuse Workflow: the saved values carry a margin that leaves
+    headroom for activations beyond the calibration maximum; an element past
+    that headroom is clamped to +-448 and counted here). A quotient of exactly
+    448 is not clamped."""
+    x = bf16_to_f32(bits)
+    d = np.float32(descale)
+    with np.errstate(over="ignore"):
+        y = (x / d).astype(np.float32)
+    return int(np.count_nonzero(np.abs(y) > e4m3.E4M3_MAX))
