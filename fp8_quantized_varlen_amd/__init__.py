@@ -21,19 +21,23 @@ __all__ = [
     "LIB_PATH", "FP8VIT_DYNAMIC", "FP8VIT_STATIC", "Fp8VitError",
     "state_bytes", "new_state", "state_init", "state_set_static", "scales_update",
     "quantize_qkv", "attn_varlen", "attn_varlen_fp8out", "attn_workspace_bytes", "attn_workspace",
-    "attn_varlen_ws", "attn_varlen_noalloc", "quantize_qkv_mx", "attn_varlen_mx", "state_read", "state_write", "calibrated_values",
+    "attn_varlen_ws", "attn_varlen_noalloc", "quantize_qkv_mx", "attn_varlen_mx", "state_read", "state_write",
+    "state_set_flags", "check_cu_seqlens", "FP8VIT_FLAG_COUNT_SATURATION", "calibrated_values",
     "load_static_scales", "save_static_scales", "status_str",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8vit.so")
 FP8VIT_DYNAMIC = 0
 FP8VIT_STATIC = 1
+FP8VIT_FLAG_COUNT_SATURATION = 1
+FP8VIT_CU_FIRST_NOT_ZERO, FP8VIT_CU_DECREASING, FP8VIT_CU_LAST_NOT_T, FP8VIT_CU_LONGER_THAN_MAX = 1, 2, 4, 8
 _MODES = {"dynamic": FP8VIT_DYNAMIC, "static": FP8VIT_STATIC}
 
 class _StateView(ctypes.Structure):
     _fields_ = [("ring", (ctypes.c_float * 16) * 3), ("count", ctypes.c_uint32),
                 ("static_values", ctypes.c_float * 3), ("descale_used", ctypes.c_float * 3),
-                ("amax_last", ctypes.c_float * 3), ("flags", ctypes.c_uint32)]
+                ("amax_last", ctypes.c_float * 3), ("flags", ctypes.c_uint32), ("cu_check", ctypes.c_uint32),
+                ("saturated", ctypes.c_uint64 * 3)]
 
 
 _vp, _i32, _i64, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
@@ -43,6 +47,8 @@ _SIGS = {
     "fp8vit_load_static_scales": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_char_p, ctypes.POINTER(_f32)]),
     "fp8vit_state_set_static": (ctypes.c_int, [_vp, ctypes.POINTER(_f32), _vp]),
     "fp8vit_scales_update": (ctypes.c_int, [_vp, _vp, _vp]),
+    "fp8vit_state_set_flags": (ctypes.c_int, [_vp, ctypes.c_uint32, _vp]),
+    "fp8vit_check_cu_seqlens": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp]),
     "fp8vit_quantize_qkv": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32,
                                            _vp, _vp, _vp, _vp, _vp]),
     "fp8vit_attn_varlen": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
@@ -440,6 +446,8 @@ def state_read(state: torch.Tensor) -> dict:
         "descale_used": list(view.descale_used),
         "amax_last": list(view.amax_last),
         "flags": int(view.flags),
+        "cu_check": int(view.cu_check),
+        "saturated": [int(x) for x in view.saturated],
     }
 
 
@@ -454,9 +462,31 @@ def state_write(state: torch.Tensor, snapshot: dict) -> None:
         view.amax_last[x] = float(snapshot["amax_last"][x])
     view.count = int(snapshot["count"])
     view.flags = int(snapshot.get("flags", 0))
+    view.cu_check = int(snapshot.get("cu_check", 0))
+    for x, n in enumerate(snapshot.get("saturated", (0, 0, 0))):
+        view.saturated[x] = int(n)
     state = _state_tensor(state)
     _check("fp8vit_state_write", _lib.fp8vit_state_write(_ptr(state), ctypes.byref(view),
                                                          _stream(_same_gpu(state=state))))
+
+
+def state_set_flags(state: torch.Tensor, flags: int) -> None:
+    """Set the state's option bits (FP8VIT_FLAG_COUNT_SATURATION) and restart the
+    saturation counts; state_read reports them under "saturated"."""
+    state = _state_tensor(state)
+    _check("fp8vit_state_set_flags",
+           _lib.fp8vit_state_set_flags(_ptr(state), int(flags), _stream(_same_gpu(state=state))))
+
+
+def check_cu_seqlens(cu_seqlens: torch.Tensor, total_tokens: int, max_seqlen: int, state: torch.Tensor) -> None:
+    """Check cu_seqlens on the device; state_read(state)["cu_check"] then holds the
+    FP8VIT_CU_* bits of the conditions it violates (0: valid)."""
+    cu_seqlens = _cu_seqlens(cu_seqlens, int(total_tokens))
+    state = _state_tensor(state)
+    dev = _same_gpu(cu_seqlens=cu_seqlens, state=state)
+    _check("fp8vit_check_cu_seqlens",
+           _lib.fp8vit_check_cu_seqlens(_ptr(cu_seqlens), cu_seqlens.numel() - 1, int(total_tokens),
+                                        int(max_seqlen), _ptr(state), _stream(dev)))
 
 
 def calibrated_values(state: torch.Tensor, margin: float = 1.5) -> Tuple[float, float, float]:

@@ -43,6 +43,21 @@ fp8vit_status fp8vit_scales_update(void* d_state, const float* d_amax_qkv, void*
   return from_hip(fp8vit::launch_scales_update(static_cast<DevState*>(d_state), d_amax_qkv, as_stream(stream)));
 }
 
+fp8vit_status fp8vit_state_set_flags(void* d_state, uint32_t flags, void* stream) {
+  if (!d_state || (flags & ~FP8VIT_FLAG_COUNT_SATURATION) != 0u) return FP8VIT_ERR_INVALID_ARGUMENT;
+  if (!aligned(d_state, 256)) return FP8VIT_ERR_UNSUPPORTED;
+  return from_hip(fp8vit::launch_state_set_flags(static_cast<DevState*>(d_state), flags, as_stream(stream)));
+}
+
+fp8vit_status fp8vit_check_cu_seqlens(const int32_t* d_cu_seqlens, int32_t num_segments, int32_t total_tokens,
+                                      int32_t max_seqlen, void* d_state, void* stream) {
+  if (!d_cu_seqlens || !d_state || num_segments < 0 || total_tokens < 0 || max_seqlen < 0)
+    return FP8VIT_ERR_INVALID_ARGUMENT;
+  if (!aligned(d_state, 256) || !aligned(d_cu_seqlens, 4)) return FP8VIT_ERR_UNSUPPORTED;
+  return from_hip(fp8vit::launch_check_cu_seqlens(d_cu_seqlens, num_segments, total_tokens, max_seqlen,
+                                                  static_cast<DevState*>(d_state), as_stream(stream)));
+}
+
 namespace {
 
 // Validation and launch of the per-tensor quantize passes; quant_mask selects
@@ -152,6 +167,7 @@ fp8vit_status attn_common(const void* q8, const void* k8, const void* v8, const 
   a.H = num_heads;
   a.ntiles_ub = (int32_t)ntiles;
   a.tensor_bytes = (uint32_t)((int64_t)total_tokens * row);
+  a.T = total_tokens;
   a.st = static_cast<const DevState*>(d_state);
   a.out = out_fp8 ? nullptr : static_cast<uint16_t*>(out);
   a.out8 = out_fp8 ? static_cast<uint8_t*>(out) : nullptr;
@@ -268,12 +284,15 @@ fp8vit_status fp8vit_state_read(const void* d_state, fp8vit_state_view* out, voi
     out->amax_last[i] = h.amax_last[i];
   }
   out->flags = h.flags;
+  out->cu_check = h.cu_check;
+  for (int i = 0; i < 3; ++i) out->saturated[i] = h.saturated[i];
   return FP8VIT_OK;
 }
 
 fp8vit_status fp8vit_state_write(void* d_state, const fp8vit_state_view* in, void* stream) {
   if (!d_state || !in) return FP8VIT_ERR_INVALID_ARGUMENT;
   if (!aligned(d_state, 256)) return FP8VIT_ERR_UNSUPPORTED;
+  if ((in->flags & ~FP8VIT_FLAG_COUNT_SATURATION) != 0u) return FP8VIT_ERR_INVALID_ARGUMENT;
   auto nonneg = [](float x) { return std::isfinite(x) && x >= 0.0f; };
   for (int x = 0; x < 3; ++x) {
     for (int i = 0; i < FP8VIT_RING_SLOTS; ++i)
@@ -294,6 +313,8 @@ fp8vit_status fp8vit_state_write(void* d_state, const fp8vit_state_view* in, voi
     h.amax_last[i] = in->amax_last[i];
   }
   h.flags = in->flags;
+  h.cu_check = in->cu_check;
+  for (int i = 0; i < 3; ++i) h.saturated[i] = in->saturated[i];
   hipError_t e = hipMemcpyAsync(d_state, &h, sizeof(DevState), hipMemcpyHostToDevice, as_stream(stream));
   if (e != hipSuccess) return FP8VIT_ERR_HIP;
   // `h` lives on this stack frame: wait for the copy before returning.

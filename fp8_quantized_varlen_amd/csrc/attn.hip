@@ -101,6 +101,14 @@ template <> struct Shape<128, true> {
   static constexpr bool XT = false, P16 = true;
 };
 
+// Segment i of the packed batch, clamped to [0, T]: a cu_seqlens that does
+// not describe the batch (fp8vit_check_cu_seqlens tells) can leave output rows
+// unwritten but never makes a kernel address memory outside the tensors.
+__device__ __forceinline__ void segment_bounds(const AttnArgs& a, int i, int& b0, int& b1) {
+  b0 = min(max(a.cu[i], 0), a.T);
+  b1 = min(max(a.cu[i + 1], b0), a.T);
+}
+
 // LDS placement of a tile. S^T block t (0..7) row i16 is key
 // 32 (i16 / 4) + 4 t + i16 % 4 (k_block_key); its A operand lane (g, i16)
 // holds d bytes 32 g .. 32 g + 31 of that key, as two 16-byte reads.
@@ -306,7 +314,8 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, WIDE>::MIN_WAVES_PER_EU))) void attn
   if (h >= a.H) return;
   int s0 = 0, L = -1;
   for (int i = 0; i < a.nseg; ++i) {
-    const int b0 = a.cu[i], b1 = a.cu[i + 1];
+    int b0, b1;
+    segment_bounds(a, i, b0, b1);
     const int n = (b1 - b0 + kBM - 1) / kBM;
     if (tile < n) { s0 = b0; L = b1 - b0; break; }
     tile -= n;
@@ -1043,7 +1052,8 @@ __global__ __launch_bounds__(2 * kSplitQueries) void attn_split_combine_kernel(A
   if (h >= a.H) return;
   int s0 = 0, L = -1;
   for (int i = 0; i < a.nseg; ++i) {
-    const int b0 = a.cu[i], b1 = a.cu[i + 1];
+    int b0, b1;
+    segment_bounds(a, i, b0, b1);
     const int n = (b1 - b0 + BM - 1) / BM;
     if (tile < n) { s0 = b0; L = b1 - b0; break; }
     tile -= n;
@@ -1143,7 +1153,8 @@ void attn_w32_kernel(AttnArgs a) {
   if (h >= a.H) return;
   int s0 = 0, L = -1;
   for (int i = 0; i < a.nseg; ++i) {
-    const int b0 = a.cu[i], b1 = a.cu[i + 1];
+    int b0, b1;
+    segment_bounds(a, i, b0, b1);
     const int n = (b1 - b0 + BM - 1) / BM;
     if (tile < n) { s0 = b0; L = b1 - b0; break; }
     tile -= n;

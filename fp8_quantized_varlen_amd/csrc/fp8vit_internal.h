@@ -30,14 +30,17 @@ struct alignas(256) DevState {
   float static_values[3];            // static q/k/v values (margin included)
   float descale_used[3];             // descales of the last quantize / update
   float amax_last[3];                // amax of the last dynamic forward
-  uint32_t flags;                    // reserved: 0
+  uint32_t flags;                    // FP8VIT_FLAG_* bits (fp8vit_state_set_flags)
   uint32_t pending;                  // 1: pending_amax still has to be pushed
   float pending_amax[3];
-  uint32_t reserved0[65];
+  uint32_t cu_check;                 // FP8VIT_CU_* bits of the last fp8vit_check_cu_seqlens
+  unsigned long long saturated[3];   // elements clamped at +-448 (with FP8VIT_FLAG_COUNT_SATURATION)
+  uint32_t reserved0[58];
   uint32_t amax_part[kAmaxSlots][4];  // amax pass block b: |q|, |k|, |v| maxima (bf16 magnitude bits)
 };
 constexpr size_t kStateViewBytes = 512;   // the reported part, before the partial maxima
 static_assert(offsetof(DevState, amax_part) == kStateViewBytes, "state layout");
+static_assert(offsetof(DevState, saturated) == 256, "state layout");
 static_assert(sizeof(DevState) == 512 + 16 * kAmaxSlots, "state layout");
 
 // Compute units of the current device (cached per device; 0 on error).
@@ -50,6 +53,9 @@ constexpr float kDescaleFloor = 1e-10f;
 hipError_t launch_state_init(DevState* st, hipStream_t s);
 hipError_t launch_state_set_static(DevState* st, float q, float k, float v, hipStream_t s);
 hipError_t launch_scales_update(DevState* st, const float* d_amax, hipStream_t s);
+hipError_t launch_state_set_flags(DevState* st, uint32_t flags, hipStream_t s);
+hipError_t launch_check_cu_seqlens(const int32_t* cu, int32_t nseg, int32_t total_tokens, int32_t max_seqlen,
+                                   DevState* st, hipStream_t s);
 
 struct QuantArgs {
   const uint16_t* x[3];
@@ -75,6 +81,7 @@ struct AttnArgs {
   int32_t H;
   int32_t ntiles_ub;     // upper bound on query tiles per head (set by launch_attn)
   uint32_t tensor_bytes; // T * H * d: bytes of each of q8, k8, v8
+  int32_t T;             // tokens (every segment is clamped to [0, T])
   const DevState* st;
   uint16_t* out;           // bf16 output (out8 == nullptr)
   uint8_t* out8;           // e4m3 output, or nullptr

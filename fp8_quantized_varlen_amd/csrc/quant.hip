@@ -55,10 +55,12 @@ constexpr int kAmaxUnroll = 4;
 __device__ __forceinline__ uint32_t bf16_lo(uint32_t w) { return w << 16; }
 __device__ __forceinline__ uint32_t bf16_hi(uint32_t w) { return w & 0xffff0000u; }
 
-// r = RN64(1 / descale), see the header comment.
+// r = RN64(1 / descale), see the header comment: the fp32 quotient x / descale.
+__device__ __forceinline__ float quotient(uint32_t fbits, double r) {
+  return (float)((double)__uint_as_float(fbits) * r);
+}
 __device__ __forceinline__ float quant_value(uint32_t fbits, double r) {
-  const float q = (float)((double)__uint_as_float(fbits) * r);
-  return __builtin_amdgcn_fmed3f(q, -kFp8Max, kFp8Max);
+  return __builtin_amdgcn_fmed3f(quotient(fbits, r), -kFp8Max, kFp8Max);
 }
 
 // 8 bf16 (one 16-byte chunk) -> 8 e4m3 codes (8 bytes), element order kept.
@@ -72,6 +74,19 @@ __device__ __forceinline__ uint2 quant_chunk(uint4 w, double r) {
                                                false);
   b = __builtin_amdgcn_cvt_pk_fp8_f32(quant_value(bf16_lo(w.w), r), quant_value(bf16_hi(w.w), r), b, true);
   return make_uint2(a, b);
+}
+
+// Elements of the chunk whose quotient exceeds 448 in magnitude: the ones the
+// clamp changes (the same quotients quant_chunk forms).
+__device__ __forceinline__ uint32_t chunk_saturated(uint4 w, double r) {
+  uint32_t n = 0;
+  const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    n += fabsf(quotient(bf16_lo(v[i]), r)) > kFp8Max ? 1u : 0u;
+    n += fabsf(quotient(bf16_hi(v[i]), r)) > kFp8Max ? 1u : 0u;
+  }
+  return n;
 }
 
 // Largest |x| of the chunk as 15-bit bf16 magnitude bits (finite inputs:
@@ -124,9 +139,10 @@ __device__ __forceinline__ void load3(const QuantArgs& a, uint32_t c, uint32_t n
 // prologue), and the next chunk's loads are issued before the current one is
 // converted and stored. Otherwise each chunk is loaded, converted and stored
 // in turn (`w` is scratch).
-template <bool CONTIG, bool NT, bool PRELOADED>
+// SAT: also count, per tensor, the elements the clamp changes (into sat[3]).
+template <bool CONTIG, bool NT, bool PRELOADED, bool SAT>
 __device__ __forceinline__ void quantize_all(const QuantArgs& a, uint32_t n8, const double* r, uint32_t gtid,
-                                             uint32_t gstride, uint4 w[3]) {
+                                             uint32_t gstride, uint4 w[3], uint32_t* sat) {
   for (uint32_t c = gtid; c < n8; c += gstride) {
     uint4 cur[3];
     if (PRELOADED) {
@@ -137,8 +153,12 @@ __device__ __forceinline__ void quantize_all(const QuantArgs& a, uint32_t n8, co
       load3<CONTIG, NT>(a, c, n8, cur);
     }
 #pragma unroll
-    for (int x = 0; x < 3; ++x)
-      if (a.quant_mask >> x & 1u) st8<NT>(reinterpret_cast<uint2*>(a.y[x]) + c, quant_chunk(cur[x], r[x]));
+    for (int x = 0; x < 3; ++x) {
+      if (a.quant_mask >> x & 1u) {
+        st8<NT>(reinterpret_cast<uint2*>(a.y[x]) + c, quant_chunk(cur[x], r[x]));
+        if (SAT) sat[x] += chunk_saturated(cur[x], r[x]);
+      }
+    }
   }
 }
 
@@ -186,6 +206,26 @@ __device__ __forceinline__ void block_max3(uint32_t m[3], uint32_t (*red)[3]) {
   }
 }
 
+__device__ __forceinline__ void block_sum3(uint32_t n[3], uint32_t (*red)[3]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int x = 0; x < 3; ++x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) n[x] += (uint32_t)__shfl_xor((int)n[x], off, 64);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int x = 0; x < 3; ++x) red[wave][x] = n[x];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < 3; ++x) {
+    n[x] = red[0][x];
+#pragma unroll
+    for (int w = 1; w < kQuantThreads / 64; ++w) n[x] += red[w][x];
+  }
+}
+
 // Quantize pass. Static mode: the descales come from the stored static
 // values (block 0 records them). Dynamic mode: every block reduces the amax
 // pass's per-block maxima to this forward's amax and takes the descales from
@@ -230,7 +270,19 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(QuantArgs a) {
   }
   __syncthreads();
   const double r[3] = {rcp[0], rcp[1], rcp[2]};
-  quantize_all<CONTIG, DYNAMIC, DYNAMIC>(a, n8, r, gtid, gstride, w);
+  if ((st->flags & FP8VIT_FLAG_COUNT_SATURATION) != 0u) {
+    // Diagnostic: count the clamped elements; one atomic add per tensor and workgroup.
+    uint32_t sat[3] = {0u, 0u, 0u};
+    quantize_all<CONTIG, DYNAMIC, DYNAMIC, true>(a, n8, r, gtid, gstride, w, sat);
+    block_sum3(sat, red);
+    if (threadIdx.x == 0) {
+#pragma unroll
+      for (int x = 0; x < 3; ++x)
+        if (sat[x] != 0u) atomicAdd(&st->saturated[x], (unsigned long long)sat[x]);
+    }
+  } else {
+    quantize_all<CONTIG, DYNAMIC, DYNAMIC, false>(a, n8, r, gtid, gstride, w, nullptr);
+  }
 }
 
 // Amax pass of dynamic mode. Each block reduces its chunks of Q, K and V and

@@ -56,6 +56,15 @@ typedef enum fp8vit_status {
 
 #define FP8VIT_RING_SLOTS 16
 
+/* Option bits of a state (fp8vit_state_set_flags). */
+#define FP8VIT_FLAG_COUNT_SATURATION 1u /* quantize passes count clamped elements */
+
+/* Bits of fp8vit_state_view.cu_check (fp8vit_check_cu_seqlens). */
+#define FP8VIT_CU_FIRST_NOT_ZERO 1u   /* cu_seqlens[0] != 0 */
+#define FP8VIT_CU_DECREASING 2u       /* cu_seqlens[i+1] < cu_seqlens[i] for some i */
+#define FP8VIT_CU_LAST_NOT_T 4u       /* cu_seqlens[num_segments] != total_tokens */
+#define FP8VIT_CU_LONGER_THAN_MAX 8u  /* a segment longer than max_seqlen */
+
 /* Host snapshot of one layer's scale state (see fp8vit_state_read). */
 typedef struct fp8vit_state_view {
   float ring[3][FP8VIT_RING_SLOTS]; /* observed amax of q, k, v; zeros when unused */
@@ -63,7 +72,9 @@ typedef struct fp8vit_state_view {
   float static_values[3];           /* values given to fp8vit_state_set_static */
   float descale_used[3];            /* descales of the last quantize (or scales_update) */
   float amax_last[3];               /* amax observed by the last dynamic forward */
-  uint32_t flags;                   /* reserved: 0 */
+  uint32_t flags;                   /* FP8VIT_FLAG_* bits; 0 after fp8vit_state_init */
+  uint32_t cu_check;                /* FP8VIT_CU_* bits of the last fp8vit_check_cu_seqlens */
+  uint64_t saturated[3];            /* q, k, v elements clamped at +-448 since the flag was set */
 } fp8vit_state_view;
 
 /* Bytes of device memory one layer's state needs. The caller allocates it
@@ -120,6 +131,37 @@ fp8vit_status fp8vit_state_set_static(void* d_state, const float values_qkv[3], 
  * Source: vLLM page "FP8 ViT Encoder Attention", Usage; atrex-bench operator
  * #025 "per_token_group_quant_fp8", Reference Implementation. */
 fp8vit_status fp8vit_scales_update(void* d_state, const float* d_amax_qkv, void* stream);
+
+/* Set the option bits of a state (FP8VIT_FLAG_*; other bits:
+ * ERR_INVALID_ARGUMENT) and restart the saturation counts from zero.
+ * With FP8VIT_FLAG_COUNT_SATURATION, every per-tensor quantize pass (of
+ * fp8vit_quantize_qkv, and the V pass of fp8vit_quantize_qkv_mx) adds to
+ * saturated[q, k, v] the number of elements whose fp32 quotient x / descale
+ * is larger than 448 in magnitude, i.e. the elements the clamp changes (one
+ * 64-bit atomic add per workgroup and tensor); without it the passes do not
+ * count. Block-scaled Q and K never clamp (their block scale is at least the
+ * block amax / 448). Asynchronous, one small kernel.
+ * Errors: ERR_INVALID_ARGUMENT (null state, unknown bits), ERR_UNSUPPORTED
+ * (state not 256-byte aligned), ERR_HIP.
+ * Source: vLLM page "FP8 ViT Encoder Attention", Calibrate-Once Reuse
+ * Workflow (the saved values carry a margin that leaves headroom for
+ * activations beyond the calibration maximum; the count shows when it does
+ * not). */
+fp8vit_status fp8vit_state_set_flags(void* d_state, uint32_t flags, void* stream);
+
+/* Check a packed batch description on the device and write the FP8VIT_CU_*
+ * bits of the conditions it violates (0 when valid) into the state's
+ * cu_check, which fp8vit_state_read reports. d_cu_seqlens: num_segments + 1
+ * int32 entries (device). The attention kernels themselves clamp every
+ * segment to [0, total_tokens], so an invalid cu_seqlens gives unspecified
+ * output rows but no access outside the tensors; this check is the way to
+ * tell. Asynchronous, one workgroup.
+ * Errors: ERR_INVALID_ARGUMENT (null pointer, num_segments, total_tokens or
+ * max_seqlen < 0), ERR_UNSUPPORTED (state not 256-byte aligned), ERR_HIP.
+ * Source: vLLM page "FP8 ViT Encoder Attention", note on ROCm (packed
+ * variable-length batches described by cumulative segment boundaries). */
+fp8vit_status fp8vit_check_cu_seqlens(const int32_t* d_cu_seqlens, int32_t num_segments, int32_t total_tokens,
+                                      int32_t max_seqlen, void* d_state, void* stream);
 
 /* Quantize Q, K and V to e4m3: one kernel launch in static mode, two in
  * dynamic mode.
@@ -331,13 +373,15 @@ fp8vit_status fp8vit_attn_varlen_fp8out(const void* q8, const void* k8, const vo
 fp8vit_status fp8vit_state_read(const void* d_state, fp8vit_state_view* out, void* stream);
 
 /* Synchronous write of a whole state, the inverse of fp8vit_state_read: ring,
- * count, static values, last descales, last amax and flags are taken from
- * `in`; the internal atomic-max scratch and arrival counter are cleared as by
- * fp8vit_state_init. With it a calibration or a dynamic ring can be saved and
- * resumed: the forwards that follow behave as they would have in the process
- * that read the state. Ring, static, descale and amax entries must be finite
- * and >= 0 (else ERR_INVALID_ARGUMENT). Copies on `stream` and waits for it,
- * so it is not for graph capture.
+ * count, static values, last descales, last amax, flags, cu_check and the
+ * saturation counts are taken from `in`; the amax pass's partial maxima are
+ * cleared as by fp8vit_state_init, and no push is pending (a view from
+ * fp8vit_state_read already has a pending push applied). With it a
+ * calibration or a dynamic ring can be saved and resumed: the forwards that
+ * follow behave as they would have in the process that read the state. Ring,
+ * static, descale and amax entries must be finite and >= 0, and flags only
+ * FP8VIT_FLAG_* bits (else ERR_INVALID_ARGUMENT). Copies on `stream` and
+ * waits for it, so it is not for graph capture.
  * Source: vLLM page "FP8 ViT Encoder Attention", Usage (the ring carries over
  * from forward to forward, so resuming it needs its whole contents). */
 fp8vit_status fp8vit_state_write(void* d_state, const fp8vit_state_view* in, void* stream);

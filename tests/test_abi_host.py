@@ -29,7 +29,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -138,6 +138,29 @@ def test_argument_validation_before_any_hip_call(lib):
         arr[i] = bad
         assert w(fake, ctypes.addressof(view), null) == 1, (field, i)
         arr[i] = 0.0
+    view.flags = 2                      # not an FP8VIT_FLAG_* bit
+    assert w(fake, ctypes.addressof(view), null) == 1
+    view.flags = 0
+    sf = lib.fp8vit_state_set_flags
+    sf.argtypes = [vp, ctypes.c_uint32, vp]
+    assert sf(null, 1, null) == 1 and sf(fake, 2, null) == 1 and sf(fake, 0xffffffff, null) == 1
+    assert sf(vp(0x10010), 1, null) == 2
+    cc = lib.fp8vit_check_cu_seqlens
+    cc.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp]
+    assert cc(null, 1, 10, 10, fake, null) == 1 and cc(fake, 1, 10, 10, null, null) == 1
+    assert cc(fake, -1, 10, 10, fake, null) == 1 and cc(fake, 1, -1, 10, fake, null) == 1
+    assert cc(fake, 1, 10, -1, fake, null) == 1
+    assert cc(fake, 1, 10, 10, vp(0x10010), null) == 2 and cc(vp(0x10002), 1, 10, 10, fake, null) == 2
+
+
+def test_state_view_layout():
+    """The binding's view structure has the C layout the header gives (natural
+    alignment: the 64-bit counts start at byte 240)."""
+    from fp8_quantized_varlen_amd import _StateView
+    off = {name: getattr(_StateView, name).offset for name, _ in _StateView._fields_}
+    assert off == {"ring": 0, "count": 192, "static_values": 196, "descale_used": 208, "amax_last": 220,
+                   "flags": 232, "cu_check": 236, "saturated": 240}
+    assert ctypes.sizeof(_StateView) == 264
 
 
 def load(lib, path, layer):
