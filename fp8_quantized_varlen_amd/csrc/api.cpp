@@ -302,7 +302,7 @@ fp8vit_status fp8vit_state_write(void* d_state, const fp8vit_state_view* in, voi
   }
   // No push is pending, and the partial maxima start from zero, as after
   // fp8vit_state_init.
-  static_assert(sizeof(DevState) <= 32768, "state copied through the stack");
+  static_assert(sizeof(DevState) <= 65536, "state copied through the stack");
   DevState h;
   std::memset(&h, 0, sizeof(h));
   std::memcpy(h.ring, in->ring, sizeof(h.ring));

@@ -10,20 +10,24 @@
 
 namespace fp8vit {
 
-// Blocks of the amax pass: at most this many per-block partial maxima fit in
-// the state.
+// Workgroups of the first dynamic pass: at most this many per-block partials
+// fit in the state.
 constexpr int kAmaxSlots = 1024;
 
 // Per-layer device state. The caller allocates fp8vit_state_bytes() bytes.
 // The first 512 bytes hold what fp8vit_state_read reports (plus the pending
-// ring push); the rest is the amax pass's per-block partial maxima.
+// ring push and the first dynamic pass's window); the rest is that pass's
+// per-block partials (amax, and clamp counts when they are counted).
 //
-// Dynamic bookkeeping is split over the two launches of a forward: the
-// quantize pass of forward n derives its descales from the ring and this
-// forward's amax and records that amax as pending (it cannot push it itself:
-// its other workgroups are still reading the ring); the amax pass of forward
-// n+1 (or fp8vit_scales_update) first pushes the pending amax into the ring.
-// fp8vit_state_read applies a pending push to the view it returns.
+// Dynamic bookkeeping is split over the two launches of a forward. Pass 1
+// reads the ring (with the previous forward's pending push applied in its
+// reading, not written) and quantizes with the window maximum over the other
+// 15 slots, recording per-block partial maxima. Pass 2 reduces them to this
+// forward's amax; one of its threads pushes the previous pending amax and
+// records this one as pending (no other thread reads the ring in pass 2);
+// every workgroup re-quantizes its share of a tensor whose amax raised the
+// window (and so its descale). fp8vit_scales_update pushes a pending amax
+// first, and fp8vit_state_read applies one to the view it returns.
 struct alignas(256) DevState {
   float ring[3][FP8VIT_RING_SLOTS];  // observed amax of q, k, v
   uint32_t count;                    // dynamic forwards pushed into the ring
@@ -35,13 +39,15 @@ struct alignas(256) DevState {
   float pending_amax[3];
   uint32_t cu_check;                 // FP8VIT_CU_* bits of the last fp8vit_check_cu_seqlens
   unsigned long long saturated[3];   // elements clamped at +-448 (with FP8VIT_FLAG_COUNT_SATURATION)
-  uint32_t reserved0[58];
-  uint32_t amax_part[kAmaxSlots][4];  // amax pass block b: |q|, |k|, |v| maxima (bf16 magnitude bits)
+  float win_other[3];                // dynamic pass 1: window max over the other 15 ring slots
+  uint32_t reserved0[55];
+  uint32_t amax_part[kAmaxSlots][4];  // dynamic pass 1, block b: |q|, |k|, |v| maxima (bf16 magnitude bits)
+  uint32_t sat_part[kAmaxSlots][4];   // dynamic pass 1, block b: clamped q, k, v elements (flag set)
 };
-constexpr size_t kStateViewBytes = 512;   // the reported part, before the partial maxima
+constexpr size_t kStateViewBytes = 512;   // the reported part, before the per-block partials
 static_assert(offsetof(DevState, amax_part) == kStateViewBytes, "state layout");
 static_assert(offsetof(DevState, saturated) == 256, "state layout");
-static_assert(sizeof(DevState) == 512 + 16 * kAmaxSlots, "state layout");
+static_assert(sizeof(DevState) == 512 + 32 * kAmaxSlots, "state layout");
 
 // Compute units of the current device (cached per device; 0 on error).
 int device_cus();
@@ -63,7 +69,7 @@ struct QuantArgs {
   uint8_t* y[3];
   int32_t T;
   int32_t row8;   // H*d/8 (16-byte chunks per token row)
-  int32_t amax_blocks;  // workgroups of the amax pass (partial maxima to reduce)
+  int32_t amax_blocks;  // workgroups of dynamic pass 1 (partials to reduce)
   uint32_t quant_mask;  // tensors the quantize pass writes (bit 0 q, 1 k, 2 v)
   DevState* st;
 };

@@ -16,16 +16,23 @@
 // the ~10 of a correctly rounded fp32 division.
 //
 // Dynamic mode (vLLM page "FP8 ViT Encoder Attention", Usage): the amax of
-// each whole tensor is reduced first, pushed into the 16-slot ring, and the
-// window maximum sets this forward's descale. Two launches: the amax pass
-// (per-block partial maxima in the state) and the quantize pass, whose every
-// block reduces those partials and takes its descales from the ring and this
-// forward's amax; the push of that amax into the ring is left pending in the
-// state and done by the next forward's amax pass (see DevState). A single cooperative launch
-// with a grid-wide barrier between the passes reads the input once, but on
-// MI355X it measured slower at every size: the cooperative launch itself adds
-// ~17 us and a barrier across eight XCDs costs several device-scope atomic
-// round trips, against ~7 us for re-reading 57 MB (L = 8192, 16 heads, d = 72).
+// each whole tensor joins the 16-slot ring, and the window maximum sets this
+// forward's descale. Two launches, one pass over the input in the usual case:
+//   pass 1 quantizes with the descale of the window over the other 15 slots
+//     (known before the pass) and records per-block partial maxima;
+//   pass 2 reduces them to this forward's amax. The true descale is that of
+//     max(window, amax); where it equals pass 1's (the amax did not raise the
+//     window, or raised it without changing the fp32 descale) the codes are
+//     already the right ones, bit for bit, and pass 2 only does the
+//     bookkeeping. Otherwise its workgroups quantize that tensor again.
+// Once the ring is full of like amaxes (steady state) a tensor is redone only
+// when its amax is the largest of the 16, about one forward in 16; the first
+// forward always redoes (empty ring). The ring push of this forward's amax is
+// left pending in the state and done by the next forward's pass 2 (see
+// DevState). A single cooperative launch with a grid-wide barrier between an
+// amax pass and the quantize pass measured slower on MI355X at every size
+// (the cooperative launch itself adds ~17 us, and a barrier across eight XCDs
+// costs several device-scope atomic round trips).
 //
 // Data layout: bf16 rows of H*d elements with token stride ld; every thread
 // moves 16-byte chunks (8 elements) in and 8-byte chunks out, consecutive
@@ -35,23 +42,18 @@
 
 namespace fp8vit {
 
-// Quantize pass: one 16-byte chunk of each of Q, K and V per thread and
+// Quantize passes: one 16-byte chunk of each of Q, K and V per thread and
 // iteration. Static mode: up to 16 workgroups per CU, each chunk loaded,
 // converted and stored in turn (a small grid with several chunks in flight
-// per thread measured 9-14 % slower). Dynamic mode, whose prologue reduces
-// the amax pass's partial maxima before the descales are known: up to 4
-// workgroups per CU (one resident round), the first loads issued before the
-// prologue and each next chunk loaded before the current one is stored.
+// per thread measured 9-14 % slower). Dynamic pass 1: up to 4 workgroups per
+// CU (one resident round, and at most kAmaxSlots partials), the first loads
+// issued before the prologue and each next chunk loaded before the current
+// one is stored. Dynamic pass 2: one workgroup per CU.
 constexpr int kQuantThreads = 512;
 constexpr int kGridPerCu = 16;
 constexpr int kGridPerCuDynamic = 4;
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
-// Amax pass: one workgroup per CU (at most kAmaxSlots), each thread with
-// kAmaxUnroll 16-byte chunks of each tensor in flight. Measured at L = 8192,
-// 16 heads: 1, 2 or 4 workgroups per CU and 2, 4 or 8 chunks within 5 %.
-constexpr int kAmaxBlocksPerCu = 1;
-constexpr int kAmaxUnroll = 4;
 __device__ __forceinline__ uint32_t bf16_lo(uint32_t w) { return w << 16; }
 __device__ __forceinline__ uint32_t bf16_hi(uint32_t w) { return w & 0xffff0000u; }
 
@@ -125,12 +127,14 @@ __device__ __forceinline__ void st8(uint2* p, uint2 v) {
   if (NT) __builtin_nontemporal_store(v2u{v.x, v.y}, reinterpret_cast<v2u*>(p));
   else *p = v;
 }
-template <bool CONTIG, bool NT>
+// Chunk c of each tensor (zeros past the end). ALL: every tensor (for the
+// amax); otherwise the tensors the pass writes.
+template <bool CONTIG, bool NT, bool ALL = false>
 __device__ __forceinline__ void load3(const QuantArgs& a, uint32_t c, uint32_t n8, uint4 w[3]) {
 #pragma unroll
   for (int x = 0; x < 3; ++x)
-    w[x] = (c < n8 && (a.quant_mask >> x & 1u)) ? ld16<NT>(chunk_src<CONTIG>(a.x[x], a.ld[x], a.row8, c))
-                                                : make_uint4(0, 0, 0, 0);
+    w[x] = (c < n8 && (ALL || (a.quant_mask >> x & 1u))) ? ld16<NT>(chunk_src<CONTIG>(a.x[x], a.ld[x], a.row8, c))
+                                                         : make_uint4(0, 0, 0, 0);
 }
 
 // Quantize this thread's chunks c = gtid + i * gstride of Q, K and V.
@@ -162,25 +166,28 @@ __device__ __forceinline__ void quantize_all(const QuantArgs& a, uint32_t n8, co
   }
 }
 
-// Largest |x| bits of each of Q, K, V over this thread's chunks (the same
-// chunk pattern as quantize_all), with 3 * kAmaxUnroll loads in flight.
-template <bool CONTIG>
-__device__ __forceinline__ void absmax_all(const QuantArgs& a, uint32_t n8, uint32_t gtid, uint32_t gstride,
-                                           uint32_t m[3]) {
-  m[0] = m[1] = m[2] = 0;
-  for (uint32_t base = gtid; base < n8; base += gstride * kAmaxUnroll) {
-    uint4 w[3][kAmaxUnroll];
+// Dynamic pass 1 over this thread's chunks c = gtid + i * gstride: the
+// largest |x| bits of each of Q, K and V (all three, for the ring) and the
+// codes of the tensors the pass writes, at the descales r of the window over
+// the other ring slots. `w` holds chunk gtid on entry (loaded before the
+// descales were known); each next chunk is loaded before the current one is
+// converted. SAT: also count clamped elements (into sat[3]).
+template <bool CONTIG, bool SAT>
+__device__ __forceinline__ void dyn_pass1_all(const QuantArgs& a, uint32_t n8, const double* r, uint32_t gtid,
+                                              uint32_t gstride, uint4 w[3], uint32_t m[3], uint32_t* sat) {
+  for (uint32_t c = gtid; c < n8; c += gstride) {
+    uint4 cur[3];
 #pragma unroll
-    for (int x = 0; x < 3; ++x)
+    for (int x = 0; x < 3; ++x) cur[x] = w[x];
+    load3<CONTIG, false, true>(a, c + gstride, n8, w);
 #pragma unroll
-      for (int u = 0; u < kAmaxUnroll; ++u) {
-        const uint32_t c = base + u * gstride;
-        w[x][u] = c < n8 ? *chunk_src<CONTIG>(a.x[x], a.ld[x], a.row8, c) : make_uint4(0, 0, 0, 0);
+    for (int x = 0; x < 3; ++x) {
+      m[x] = max(m[x], chunk_absmax_bits(cur[x]));
+      if (a.quant_mask >> x & 1u) {
+        st8<false>(reinterpret_cast<uint2*>(a.y[x]) + c, quant_chunk(cur[x], r[x]));
+        if (SAT) sat[x] += chunk_saturated(cur[x], r[x]);
       }
-#pragma unroll
-    for (int x = 0; x < 3; ++x)
-#pragma unroll
-      for (int u = 0; u < kAmaxUnroll; ++u) m[x] = max(m[x], chunk_absmax_bits(w[x][u]));
+    }
   }
 }
 
@@ -226,14 +233,10 @@ __device__ __forceinline__ void block_sum3(uint32_t n[3], uint32_t (*red)[3]) {
   }
 }
 
-// Quantize pass. Static mode: the descales come from the stored static
-// values (block 0 records them). Dynamic mode: every block reduces the amax
-// pass's per-block maxima to this forward's amax and takes the descales from
-// the window maximum over the ring slots other than count % 16 and that amax
-// (the ring itself is not changed here: block 0 records the amax as pending,
-// to be pushed by the next forward's amax pass).
-template <bool CONTIG, bool DYNAMIC>
-__global__ __launch_bounds__(kQuantThreads) void quant_kernel(QuantArgs a) {
+// Static quantize pass: the descales come from the stored static values
+// (block 0 records them as the descales in use).
+template <bool CONTIG>
+__global__ __launch_bounds__(kQuantThreads) void quant_static_kernel(QuantArgs a) {
   __shared__ double rcp[3];
   __shared__ uint32_t red[kQuantThreads / 64][3];
   const uint32_t gtid = blockIdx.x * kQuantThreads + threadIdx.x;
@@ -241,26 +244,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(QuantArgs a) {
   const uint32_t n8 = (uint32_t)a.T * (uint32_t)a.row8;
   DevState* st = a.st;
   uint4 w[3];
-  if (DYNAMIC) load3<CONTIG, true>(a, gtid, n8, w);   // in flight during the prologue
-  if (DYNAMIC) {
-    uint32_t m[3] = {0u, 0u, 0u};
-    for (int b = threadIdx.x; b < a.amax_blocks; b += kQuantThreads) {
-      const uint4 part = *reinterpret_cast<const uint4*>(st->amax_part[b]);
-      m[0] = max(m[0], part.x);
-      m[1] = max(m[1], part.y);
-      m[2] = max(m[2], part.z);
-    }
-    block_max3(m, red);
-    if (threadIdx.x == 0) {
-      float amax[3], d[3];
-#pragma unroll
-      for (int x = 0; x < 3; ++x) amax[x] = __uint_as_float(m[x] << 16);
-      ring_window_descales(st, st->count, amax, d);
-#pragma unroll
-      for (int x = 0; x < 3; ++x) rcp[x] = 1.0 / (double)d[x];
-      if (blockIdx.x == 0) record_pending(st, amax, d);
-    }
-  } else if (threadIdx.x == 0) {
+  if (threadIdx.x == 0) {
 #pragma unroll
     for (int x = 0; x < 3; ++x) {
       const float d = descale_from_amax(st->static_values[x]);
@@ -273,7 +257,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(QuantArgs a) {
   if ((st->flags & FP8VIT_FLAG_COUNT_SATURATION) != 0u) {
     // Diagnostic: count the clamped elements; one atomic add per tensor and workgroup.
     uint32_t sat[3] = {0u, 0u, 0u};
-    quantize_all<CONTIG, DYNAMIC, DYNAMIC, true>(a, n8, r, gtid, gstride, w, sat);
+    quantize_all<CONTIG, false, false, true>(a, n8, r, gtid, gstride, w, sat);
     block_sum3(sat, red);
     if (threadIdx.x == 0) {
 #pragma unroll
@@ -281,27 +265,153 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(QuantArgs a) {
         if (sat[x] != 0u) atomicAdd(&st->saturated[x], (unsigned long long)sat[x]);
     }
   } else {
-    quantize_all<CONTIG, DYNAMIC, DYNAMIC, false>(a, n8, r, gtid, gstride, w, nullptr);
+    quantize_all<CONTIG, false, false, false>(a, n8, r, gtid, gstride, w, nullptr);
   }
 }
 
-// Amax pass of dynamic mode. Each block reduces its chunks of Q, K and V and
-// stores the three maxima in its own slot of the state; there are no
-// atomics and no last-block step (the quantize pass reduces the slots).
-// Block 0 first pushes the amax the previous dynamic forward left pending:
-// nothing else reads the ring during this pass.
+// Dynamic pass 1: quantize at the descales of the window over the other 15
+// ring slots and leave per-block partial maxima (and clamp counts) in the
+// state. Reads the ring only; block 0 also records the window for pass 2.
 template <bool CONTIG>
-__global__ __launch_bounds__(kQuantThreads) void amax_kernel(QuantArgs a) {
+__global__ __launch_bounds__(kQuantThreads) void quant_dyn_kernel(QuantArgs a) {
+  __shared__ double rcp[3];
   __shared__ uint32_t red[kQuantThreads / 64][3];
+  __shared__ uint32_t red_sat[kQuantThreads / 64][3];
   const uint32_t gtid = blockIdx.x * kQuantThreads + threadIdx.x;
   const uint32_t gstride = gridDim.x * kQuantThreads;
   const uint32_t n8 = (uint32_t)a.T * (uint32_t)a.row8;
   DevState* st = a.st;
-  if (blockIdx.x == 0 && threadIdx.x == 0) ring_push_pending(st);
-  uint32_t m[3];
-  absmax_all<CONTIG>(a, n8, gtid, gstride, m);
+  uint4 w[3];
+  load3<CONTIG, false, true>(a, gtid, n8, w);   // in flight during the prologue
+  if (threadIdx.x < 64) {
+    // Window maximum per tensor over the ring slots other than this
+    // forward's, reading the ring as it is once the push the previous forward
+    // left pending is done (that push goes to slot count % 16 and this
+    // forward's slot is the next one). The loads are spread over wave 0 so
+    // that they are all in flight at once: lane 16 x + i holds slot i of
+    // tensor x.
+    const int lane = threadIdx.x, x = (lane >> 4) % 3, i = lane & 15;
+    const float ring = st->ring[x][i], pa = st->pending_amax[x];
+    const uint32_t count = st->count;
+    const bool pend = st->pending != 0u;
+    const uint32_t slot_p = count % FP8VIT_RING_SLOTS;
+    const uint32_t slot_this = (count + (pend ? 1u : 0u)) % FP8VIT_RING_SLOTS;
+    float v = (pend && i == (int)slot_p) ? pa : ring;
+    v = (lane < 48 && i != (int)slot_this) ? v : 0.0f;
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    if (lane < 48 && i == 0) {
+      rcp[x] = 1.0 / (double)descale_from_amax(v);
+      if (blockIdx.x == 0) st->win_other[x] = v;
+    }
+  }
+  __syncthreads();
+  const double r[3] = {rcp[0], rcp[1], rcp[2]};
+  uint32_t m[3] = {0u, 0u, 0u};
+  if ((st->flags & FP8VIT_FLAG_COUNT_SATURATION) != 0u) {
+    uint32_t sat[3] = {0u, 0u, 0u};
+    dyn_pass1_all<CONTIG, true>(a, n8, r, gtid, gstride, w, m, sat);
+    block_sum3(sat, red_sat);
+    if (threadIdx.x == 0) *reinterpret_cast<uint4*>(st->sat_part[blockIdx.x]) = make_uint4(sat[0], sat[1], sat[2], 0u);
+  } else {
+    dyn_pass1_all<CONTIG, false>(a, n8, r, gtid, gstride, w, m, nullptr);
+  }
   block_max3(m, red);
   if (threadIdx.x == 0) *reinterpret_cast<uint4*>(st->amax_part[blockIdx.x]) = make_uint4(m[0], m[1], m[2], 0u);
+}
+
+// Dynamic pass 2: every block reduces pass 1's partials to this forward's
+// amax and the true descales, max(window, amax) / 448 with the floor. Block
+// 0's first thread does the bookkeeping: the previous forward's pending push,
+// this forward's amax as pending, the descales in use and, when counting,
+// pass 1's clamp counts of the tensors that stand. A tensor whose descale
+// differs from pass 1's is quantized again by all blocks.
+template <bool CONTIG>
+__global__ __launch_bounds__(kQuantThreads) void quant_fix_kernel(QuantArgs a) {
+  __shared__ double rcp[3];
+  __shared__ uint32_t redo_sh;
+  __shared__ uint32_t red[kQuantThreads / 64][3];
+  __shared__ uint32_t red_sat[kQuantThreads / 64][3];
+  DevState* st = a.st;
+  const bool count_sat = (st->flags & FP8VIT_FLAG_COUNT_SATURATION) != 0u;
+  // Everything the bookkeeping reads, loaded before the reduction so that the
+  // loads overlap it (only block 0's first thread writes the state below).
+  float wo[3], pa[3];
+  uint32_t count = 0u, pend = 0u;
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+      wo[x] = st->win_other[x];
+      pa[x] = st->pending_amax[x];
+    }
+    count = st->count;
+    pend = st->pending;
+  }
+  uint32_t m[3] = {0u, 0u, 0u}, sat[3] = {0u, 0u, 0u};
+  for (int b = threadIdx.x; b < a.amax_blocks; b += kQuantThreads) {
+    const uint4 part = *reinterpret_cast<const uint4*>(st->amax_part[b]);
+    m[0] = max(m[0], part.x);
+    m[1] = max(m[1], part.y);
+    m[2] = max(m[2], part.z);
+    if (count_sat && blockIdx.x == 0) {
+      const uint4 sp = *reinterpret_cast<const uint4*>(st->sat_part[b]);
+      sat[0] += sp.x;
+      sat[1] += sp.y;
+      sat[2] += sp.z;
+    }
+  }
+  block_max3(m, red);
+  if (count_sat && blockIdx.x == 0) block_sum3(sat, red_sat);
+  if (threadIdx.x == 0) {
+    float amax[3], d[3];
+    uint32_t redo = 0u;
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+      amax[x] = __uint_as_float(m[x] << 16);
+      d[x] = descale_from_amax(amax[x] > wo[x] ? amax[x] : wo[x]);
+      if ((a.quant_mask >> x & 1u) && d[x] != descale_from_amax(wo[x])) redo |= 1u << x;
+      rcp[x] = 1.0 / (double)d[x];
+    }
+    redo_sh = redo;
+    if (blockIdx.x == 0) {
+      // the previous forward's pending push (ring_push_pending, from the
+      // values loaded above), then this forward's amax as pending
+      if (pend != 0u) {
+#pragma unroll
+        for (int x = 0; x < 3; ++x) st->ring[x][count % FP8VIT_RING_SLOTS] = pa[x];
+        st->count = count + 1u;
+      }
+      record_pending(st, amax, d);
+      if (count_sat) {
+#pragma unroll
+        for (int x = 0; x < 3; ++x)
+          if (!(redo >> x & 1u) && sat[x] != 0u) atomicAdd(&st->saturated[x], (unsigned long long)sat[x]);
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t redo = redo_sh;
+  if (redo == 0u) return;
+  QuantArgs ar = a;
+  ar.quant_mask = redo;
+  const double r[3] = {rcp[0], rcp[1], rcp[2]};
+  const uint32_t gtid = blockIdx.x * kQuantThreads + threadIdx.x;
+  const uint32_t gstride = gridDim.x * kQuantThreads;
+  const uint32_t n8 = (uint32_t)a.T * (uint32_t)a.row8;
+  uint4 w[3];
+  if (count_sat) {
+    uint32_t cnt[3] = {0u, 0u, 0u};
+    quantize_all<CONTIG, true, false, true>(ar, n8, r, gtid, gstride, w, cnt);
+    __syncthreads();   // red_sat may still be read by block 0's sum above
+    block_sum3(cnt, red_sat);
+    if (threadIdx.x == 0) {
+#pragma unroll
+      for (int x = 0; x < 3; ++x)
+        if ((redo >> x & 1u) && cnt[x] != 0u) atomicAdd(&st->saturated[x], (unsigned long long)cnt[x]);
+    }
+  } else {
+    quantize_all<CONTIG, true, false, false>(ar, n8, r, gtid, gstride, w, nullptr);
+  }
 }
 
 // Block-scaled (MX) e4m3 quantization of one tensor (Q or K of the
@@ -377,33 +487,30 @@ hipError_t launch_quantize(const QuantArgs& a, bool dynamic, hipStream_t s) {
   const uint64_t n8 = (uint64_t)a.T * (uint64_t)a.row8;
   uint64_t g = (n8 + (uint64_t)kQuantThreads - 1) / (uint64_t)kQuantThreads;
   if (g < 1) g = 1;
-  const uint64_t gmax = (uint64_t)cus * (dynamic ? kGridPerCuDynamic : kGridPerCu);
-  if (g > gmax) g = gmax;
-  const dim3 grid((unsigned)g), block(kQuantThreads);
-  if (dynamic) {
-    uint64_t ga = (n8 + (uint64_t)kQuantThreads * kAmaxUnroll - 1) / ((uint64_t)kQuantThreads * kAmaxUnroll);
-    if (ga < 1) ga = 1;
-    if (ga > (uint64_t)cus * kAmaxBlocksPerCu) ga = (uint64_t)cus * kAmaxBlocksPerCu;
-    if (ga > (uint64_t)kAmaxSlots) ga = kAmaxSlots;
-    const dim3 agrid((unsigned)ga);
-    QuantArgs ad = a;
-    ad.amax_blocks = (int32_t)ga;
+  const dim3 block(kQuantThreads);
+  if (!dynamic) {
+    const uint64_t gs = g < (uint64_t)cus * kGridPerCu ? g : (uint64_t)cus * kGridPerCu;
     if (contig)
-      hipLaunchKernelGGL(amax_kernel<true>, agrid, block, 0, s, ad);
+      hipLaunchKernelGGL(quant_static_kernel<true>, dim3((unsigned)gs), block, 0, s, a);
     else
-      hipLaunchKernelGGL(amax_kernel<false>, agrid, block, 0, s, ad);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (contig)
-      hipLaunchKernelGGL((quant_kernel<true, true>), grid, block, 0, s, ad);
-    else
-      hipLaunchKernelGGL((quant_kernel<false, true>), grid, block, 0, s, ad);
-  } else {
-    if (contig)
-      hipLaunchKernelGGL((quant_kernel<true, false>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((quant_kernel<false, false>), grid, block, 0, s, a);
+      hipLaunchKernelGGL(quant_static_kernel<false>, dim3((unsigned)gs), block, 0, s, a);
+    return hipGetLastError();
   }
+  uint64_t g1 = g < (uint64_t)cus * kGridPerCuDynamic ? g : (uint64_t)cus * kGridPerCuDynamic;
+  if (g1 > (uint64_t)kAmaxSlots) g1 = kAmaxSlots;
+  const uint64_t g2 = g < (uint64_t)cus ? g : (uint64_t)cus;
+  QuantArgs ad = a;
+  ad.amax_blocks = (int32_t)g1;
+  if (contig)
+    hipLaunchKernelGGL(quant_dyn_kernel<true>, dim3((unsigned)g1), block, 0, s, ad);
+  else
+    hipLaunchKernelGGL(quant_dyn_kernel<false>, dim3((unsigned)g1), block, 0, s, ad);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (contig)
+    hipLaunchKernelGGL(quant_fix_kernel<true>, dim3((unsigned)g2), block, 0, s, ad);
+  else
+    hipLaunchKernelGGL(quant_fix_kernel<false>, dim3((unsigned)g2), block, 0, s, ad);
   return hipGetLastError();
 }
 

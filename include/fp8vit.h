@@ -80,7 +80,7 @@ typedef struct fp8vit_state_view {
 /* Bytes of device memory one layer's state needs. The caller allocates it
  * (256-byte aligned) and calls fp8vit_state_init before first use. The state
  * holds the 16-slot amax ring and count, the static values, the descales in
- * use and the amax pass's reduction scratch.
+ * use and the first dynamic pass's per-block partials (33,280 bytes).
  * Source: vLLM page "FP8 ViT Encoder Attention", Usage (a 16-entry circular
  * buffer of observed Q/K/V amax drives each forward's scale) and Scale File
  * Format (per-layer static q/k/v values). */
@@ -170,10 +170,14 @@ fp8vit_status fp8vit_check_cu_seqlens(const int32_t* d_cu_seqlens, int32_t num_s
  *                of 8); base pointers 16-byte aligned.
  *   mode         FP8VIT_DYNAMIC: amax of each whole tensor (all tokens, all
  *                heads) is pushed into the ring and the descale comes from the
- *                16-slot window max including this forward (an amax pass,
- *                whose last block does the ring bookkeeping, then the
- *                quantize pass). FP8VIT_STATIC: descale from the
- *                stored static values; no amax pass, ring untouched.
+ *                16-slot window max including this forward. Pass 1 quantizes
+ *                at the descale of the other 15 slots while it reduces the
+ *                amax; pass 2 does the ring bookkeeping and quantizes a
+ *                tensor again only if its amax changed that descale (the
+ *                first forward, and in steady state about one forward in
+ *                16), so the codes are those of the window including this
+ *                forward in every case. FP8VIT_STATIC: descale from the
+ *                stored static values; no amax, ring untouched.
  *   q8, k8, v8   uint8 e4m3fn outputs, contiguous [total_tokens, H, d],
  *                16-byte aligned.
  * Per element: y = x / descale (IEEE fp32 division, nearest), clamped to
@@ -184,7 +188,8 @@ fp8vit_status fp8vit_check_cu_seqlens(const int32_t* d_cu_seqlens, int32_t num_s
  * null; dynamic mode records amax 0). Dynamic mode is two launches, not one:
  * the pages ask only that Q, K and V be quantized right before the attention
  * call, and a single cooperative launch with a grid-wide barrier measured
- * slower on MI355X at every size.
+ * slower on MI355X at every size; in the usual case the second launch reads
+ * only the first one's per-block maxima.
  * Errors: ERR_INVALID_ARGUMENT (null pointer, negative size, unknown mode,
  * ld < H*d), ERR_UNSUPPORTED (misalignment, H*d not a multiple of 8, or
  * total_tokens * H * d / 8 >= 2^31), ERR_HIP.

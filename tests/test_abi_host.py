@@ -69,7 +69,7 @@ def test_status_strings(lib):
     lib.fp8vit_status_str.restype = ctypes.c_char_p
     seen = {lib.fp8vit_status_str(i) for i in range(7)}
     assert len(seen) == 7 and lib.fp8vit_status_str(0) == b"ok"
-    assert lib.fp8vit_state_bytes() == 512 + 16 * 1024
+    assert lib.fp8vit_state_bytes() == 512 + 32 * 1024
 
 
 def test_argument_validation_before_any_hip_call(lib):

@@ -103,7 +103,7 @@ def test_state_write_then_static_and_reset():
     st = fv.new_state(dev)
     snap = {"ring": [[float(x + 16 * i) for i in range(16)] for x in range(3)], "count": 37,
             "static_values": [1.0, 2.0, 3.0], "descale_used": [0.5, 0.25, 0.125], "amax_last": [7.0, 8.0, 9.0],
-            "flags": 0}
+            "flags": 0, "cu_check": 0, "saturated": [0, 0, 0]}
     fv.state_write(st, snap)
     assert fv.state_read(st) == snap
     # a dynamic forward after the write pushes into slot 37 % 16 = 5
