@@ -117,13 +117,18 @@ fp8vit_status fp8vit_quantize_qkv_mx(const void* q, const void* k, const void* v
   const fp8vit_status st = quantize_common(q, k, v, ld_q, ld_k, ld_v, total_tokens, num_heads, head_dim, mode, q8,
                                            k8, v8, d_state, 4u, stream);
   if (st != FP8VIT_OK || total_tokens == 0) return st;
-  hipError_t e = fp8vit::launch_quantize_mx(static_cast<const uint16_t*>(q), ld_q, total_tokens, num_heads, head_dim,
-                                            static_cast<uint8_t*>(q8), static_cast<uint8_t*>(q_scales),
-                                            as_stream(stream));
-  if (e != hipSuccess) return FP8VIT_ERR_HIP;
-  e = fp8vit::launch_quantize_mx(static_cast<const uint16_t*>(k), ld_k, total_tokens, num_heads, head_dim,
-                                 static_cast<uint8_t*>(k8), static_cast<uint8_t*>(k_scales), as_stream(stream));
-  return from_hip(e);
+  fp8vit::MxArgs m;
+  m.x[0] = static_cast<const uint16_t*>(q);
+  m.x[1] = static_cast<const uint16_t*>(k);
+  m.ld[0] = ld_q;
+  m.ld[1] = ld_k;
+  m.codes[0] = static_cast<uint8_t*>(q8);
+  m.codes[1] = static_cast<uint8_t*>(k8);
+  m.scales[0] = static_cast<uint8_t*>(q_scales);
+  m.scales[1] = static_cast<uint8_t*>(k_scales);
+  m.T = total_tokens;
+  m.H = num_heads;
+  return from_hip(fp8vit::launch_quantize_mx(m, head_dim, as_stream(stream)));
 }
 
 namespace {

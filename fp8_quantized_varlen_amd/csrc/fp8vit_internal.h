@@ -74,9 +74,17 @@ struct QuantArgs {
   DevState* st;
 };
 hipError_t launch_quantize(const QuantArgs& a, bool dynamic, hipStream_t s);
-// Block-scaled e4m3 codes [T, H, d] and E8M0 scales [T, H, 4] of one bf16 tensor.
-hipError_t launch_quantize_mx(const uint16_t* x, int64_t ld, int32_t T, int32_t H, int32_t d, uint8_t* codes,
-                              uint8_t* scales, hipStream_t s);
+// Block-scaled e4m3 codes [T, H, d] and E8M0 scales [T, H, 4] of two bf16
+// tensors (Q and K), one launch.
+struct MxArgs {
+  const uint16_t* x[2];
+  int64_t ld[2];
+  uint8_t* codes[2];
+  uint8_t* scales[2];
+  int32_t T;
+  int32_t H;
+};
+hipError_t launch_quantize_mx(const MxArgs& a, int32_t d, hipStream_t s);
 
 struct AttnArgs {
   const uint8_t* q8;

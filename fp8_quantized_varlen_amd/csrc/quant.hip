@@ -417,66 +417,98 @@ __global__ __launch_bounds__(kQuantThreads) void quant_fix_kernel(QuantArgs a) {
 // Block-scaled (MX) e4m3 quantization of one tensor (Q or K of the
 // block-scaled variant; FlashInfer PR 5283 analysis, Code analysis section 1:
 // a scale per block of the head dimension from the block's amax over the
-// element format's largest value). One thread per (token, head, 32-element
-// block of head_dim; a trailing partial block is its own block):
+// element format's largest value). Per (token, head, 32-element block of
+// head_dim; a trailing partial block is its own block):
 //   s = the smallest integer with 448 * 2^s >= block amax (-127 for a zero or
 //       subnormal-only block; never above 120 for finite bf16 inputs),
 //   code_i = e4m3 RNE of clamp(x_i * 2^-s, +-448) (the product is exact),
 //   scale byte = s + 127 (E8M0), four bytes per (token, head), unused ones 0.
 // From the bf16 bits of the amax 2^E * (1 + m/128): 448 * 2^(E-8) = 1.75 * 2^E,
 // so s = E - 8 when m <= 96 (1 + m/128 <= 1.75) and E - 7 otherwise.
-__global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restrict__ x, int64_t ld, int32_t T,
-                                                       int32_t H, int32_t d, uint8_t* __restrict__ codes,
-                                                       uint8_t* __restrict__ scales) {
-  const int nb = (d + 31) / 32;
-  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t row = tid / nb;
-  const int b = (int)(tid - row * nb);
-  if (row >= (int64_t)T * H) return;
-  const int64_t t = row / H, h = row - t * H;
-  const int n8 = min(32, d - 32 * b) / 8;   // 16-byte chunks in this block (4, or 1 for head_dim 72's last)
-  const uint4* src = reinterpret_cast<const uint4*>(x + t * ld + h * d + 32 * b);
-  uint4 w[4];
-  uint32_t m = 0;
+//
+// Q and K in one launch. A wave takes kMxTiles groups of whole (token, head)
+// rows of each tensor; a group is D/8 16-byte chunks per row (hd72: 7 rows =
+// 63 chunks, lane 63 idle; hd128: 4 rows = 64), lane l on chunk l, so the
+// loads and the code stores of a wave are contiguous. All 2 * kMxTiles loads
+// of a lane are issued before any conversion. A block's maximum is the
+// maximum over its adjacent lanes (4, or 1 for hd72's third block).
+constexpr int kMxTiles = 2;
+
+template <int D>
+__device__ __forceinline__ void mx_quant_chunk(uint4 w, int lane, int jj, bool active, int64_t row,
+                                               uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int b = jj >> 2;                                   // block of this chunk
+  const int nchunks = (D == 72 && b == 2) ? 1 : 4;         // chunks in that block
+  const int g0 = lane - (jj & 3);                          // the block's first lane
+  const uint32_t m = chunk_absmax_bits(w);
+  uint32_t bm = m;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    w[c] = c < n8 ? src[c] : make_uint4(0, 0, 0, 0);
-    m = max(m, chunk_absmax_bits(w[c]));
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t o = (uint32_t)__shfl((int)m, g0 + k, 64);
+    bm = k < nchunks ? max(bm, o) : bm;
   }
-  const int efield = (int)(m >> 7), mant = (int)(m & 0x7f);
+  const int efield = (int)(bm >> 7), mant = (int)(bm & 0x7f);
   const int sexp = efield == 0 ? -127 : max(efield - 127 - 8 + (mant > 96 ? 1 : 0), -127);
-  const float r = __uint_as_float((uint32_t)(127 - sexp) << 23);   // 2^-s, a normal float for s in [-127, 120]
-  uint8_t* dst = codes + row * d + 32 * b;
+  const float rs = __uint_as_float((uint32_t)(127 - sexp) << 23);   // 2^-s, a normal float for s in [-127, 120]
+  if (!active) return;
+  const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+  uint32_t out[2];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    if (c < n8) {
-      uint32_t wv[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
-      uint32_t out[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const float y0 = __builtin_amdgcn_fmed3f(__uint_as_float(bf16_lo(wv[2 * hh])) * r, -kFp8Max, kFp8Max);
-        const float y1 = __builtin_amdgcn_fmed3f(__uint_as_float(bf16_hi(wv[2 * hh])) * r, -kFp8Max, kFp8Max);
-        const float y2 = __builtin_amdgcn_fmed3f(__uint_as_float(bf16_lo(wv[2 * hh + 1])) * r, -kFp8Max, kFp8Max);
-        const float y3 = __builtin_amdgcn_fmed3f(__uint_as_float(bf16_hi(wv[2 * hh + 1])) * r, -kFp8Max, kFp8Max);
-        int p = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
-        out[hh] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, p, true);
-      }
-      *reinterpret_cast<uint2*>(dst + 8 * c) = make_uint2(out[0], out[1]);
-    }
+  for (int hh = 0; hh < 2; ++hh) {
+    const float y0 = __builtin_amdgcn_fmed3f(__uint_as_float(bf16_lo(wv[2 * hh])) * rs, -kFp8Max, kFp8Max);
+    const float y1 = __builtin_amdgcn_fmed3f(__uint_as_float(bf16_hi(wv[2 * hh])) * rs, -kFp8Max, kFp8Max);
+    const float y2 = __builtin_amdgcn_fmed3f(__uint_as_float(bf16_lo(wv[2 * hh + 1])) * rs, -kFp8Max, kFp8Max);
+    const float y3 = __builtin_amdgcn_fmed3f(__uint_as_float(bf16_hi(wv[2 * hh + 1])) * rs, -kFp8Max, kFp8Max);
+    const int p = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+    out[hh] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, p, true);
   }
-  uint8_t* sp = scales + row * 4;
-  sp[b] = (uint8_t)(sexp + 127);
-  if (b == nb - 1)
-    for (int pb = nb; pb < 4; ++pb) sp[pb] = 0;
+  *reinterpret_cast<uint2*>(codes + row * D + 8 * jj) = make_uint2(out[0], out[1]);
+  if ((jj & 3) == 0) {
+    scales[row * 4 + b] = (uint8_t)(sexp + 127);
+    if (D == 72 && b == 2) scales[row * 4 + 3] = 0;
+  }
 }
 
-hipError_t launch_quantize_mx(const uint16_t* x, int64_t ld, int32_t T, int32_t H, int32_t d, uint8_t* codes,
-                              uint8_t* scales, hipStream_t s) {
-  const int64_t threads = (int64_t)T * H * ((d + 31) / 32);
-  if (threads == 0) return hipSuccess;
-  const int64_t blocks = (threads + 255) / 256;
+template <int D>
+__global__ __launch_bounds__(256) void mx_quant_kernel(MxArgs a) {
+  constexpr int CPR = D / 8;      // chunks per row
+  constexpr int RPW = 64 / CPR;   // rows per group
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int r = lane / CPR, jj = lane - r * CPR;   // row within a group, chunk within the row
+  const int64_t nrows = (int64_t)a.T * a.H;
+  uint4 w[2][kMxTiles];
+  int64_t rows[kMxTiles];
+  bool active[kMxTiles];
+#pragma unroll
+  for (int k = 0; k < kMxTiles; ++k) {
+    rows[k] = (wave * kMxTiles + k) * RPW + r;
+    active[k] = r < RPW && rows[k] < nrows;
+    const int64_t t = active[k] ? rows[k] / a.H : 0, h = active[k] ? rows[k] - t * a.H : 0;
+#pragma unroll
+    for (int z = 0; z < 2; ++z)
+      w[z][k] = active[k] ? *reinterpret_cast<const uint4*>(a.x[z] + t * a.ld[z] + h * D + 8 * jj)
+                          : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int z = 0; z < 2; ++z)
+#pragma unroll
+    for (int k = 0; k < kMxTiles; ++k) mx_quant_chunk<D>(w[z][k], lane, jj, active[k], rows[k], a.codes[z], a.scales[z]);
+}
+
+hipError_t launch_quantize_mx(const MxArgs& a, int32_t d, hipStream_t s) {
+  const int64_t rows = (int64_t)a.T * a.H;
+  if (rows == 0) return hipSuccess;
+  const int rpw = d == 72 ? 64 / 9 : 64 / 16;
+  const int64_t waves = (rows + (int64_t)rpw * kMxTiles - 1) / ((int64_t)rpw * kMxTiles);
+  const int64_t blocks = (waves + 3) / 4;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(mx_quant_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, ld, T, H, d, codes, scales);
+  if (d == 72)
+    hipLaunchKernelGGL(mx_quant_kernel<72>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  else if (d == 128)
+    hipLaunchKernelGGL(mx_quant_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

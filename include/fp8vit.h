@@ -314,8 +314,9 @@ fp8vit_status fp8vit_attn_varlen_noalloc(const void* q8, const void* k8, const v
  *   s_b          the smallest integer with 448 * 2^s_b >= the block's amax
  *                 (so no element saturates), -127 for a block of zeros.
  * v8, state, mode, strides, alignment and errors as fp8vit_quantize_qkv, and
- * ERR_UNSUPPORTED for head_dim other than 72 or 128. Up to four launches
- * (dynamic amax pass, V, Q, K).
+ * ERR_UNSUPPORTED for head_dim other than 72 or 128. Two launches in static
+ * mode (V; then Q and K together), three in dynamic mode (V's two passes,
+ * which also take the amax of Q and K for the ring; then Q and K).
  * Source: FlashInfer PR 5283 analysis ("experimental NVFP4 attention"), Code
  * analysis section 1 (a scale per block of the head dimension from the block
  * amax over the element format's largest value); PR 3684 analysis
