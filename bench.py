@@ -63,8 +63,9 @@ def parse():
                         "32-element block of head_dim), per-tensor V")
     p.add_argument("--graph", action="store_true",
                    help="also time the steps as one captured HIP graph (no host launch gaps)")
-    p.add_argument("--hot", action="store_true",
-                   help="also time the steps on a single input set (no rotation), reported as 'hot'")
+    p.add_argument("--no-hot", dest="hot", action="store_false",
+                   help="skip the 'hot' figure (the same steps on a single input set, no rotation), "
+                        "which is reported beside the rotated one by default")
     p.add_argument("--kernel-events-every", type=int, default=10,
                    help="bracket the quantize and attention launches with HIP events on every N-th timed step")
     p.add_argument("--calib-copy", action="store_true",
@@ -542,6 +543,10 @@ def main():
                               (" (1.5 x calibrated)" if w.mode == "static" else " (16-slot ring)"),
                    "outlier_frac": w.outlier_frac, "input_sets_rotated": n_sets},
         "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
+        # the same against the dense FP8 rate at the clock the chip held during the timed
+        # block (256 CUs x 8192 FP8 flop per clock per CU x f)
+        "pct_fp8_peak_at_measured_clock": (round(100 * value / (256 * 8192 * clk * 1e-6), 2)
+                                           if (clk := (clock_during and _pct(clock_during, 50))) else None),
         "settle": {"seconds": round(settle_s, 3), "steps": settle_steps},
         "blocks": {"n": len(block_ms), "steps_each": args.steps,
                    "median_ms_per_step": _r(_pct(block_ms, 50), 4), "p10_ms_per_step": _r(_pct(block_ms, 10), 4),
