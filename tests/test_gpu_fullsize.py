@@ -5,8 +5,8 @@ warm-ups exactly as bench.py runs them before its timed steps):
 * L=8192, 16 heads, hd72, static 1.5 x calibrated: every row of the output
   against the oracle (element by element) and against unquantized fp64;
 * L=256, 16 heads, hd72, dynamic on an empty ring (first forward): every row;
-* L=2304, 16 heads, hd72, dynamic after its 16 warm-ups: every row (this shape
-  splits the keys);
+* L=2304, 16 heads, hd72, dynamic after its 16 warm-ups: every row (the
+  workspace entry point, whose plan does not split this shape);
 * L=8192, 16 heads, hd128, dynamic after its 16 warm-ups: 2048 sampled rows
   plus the first and last row of every head.
 
