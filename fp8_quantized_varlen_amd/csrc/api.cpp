@@ -61,7 +61,7 @@ fp8vit_status fp8vit_check_cu_seqlens(const int32_t* d_cu_seqlens, int32_t num_s
 namespace {
 
 // Validation and launch of the per-tensor quantize passes; quant_mask selects
-// which of Q, K, V (bits 0, 1, 2) get codes. Dynamic mode's amax pass and ring
+// which of Q, K, V (bits 0, 1, 2) get codes. Dynamic mode's amax and ring
 // bookkeeping always cover all three tensors.
 fp8vit_status quantize_common(const void* q, const void* k, const void* v, int64_t ld_q, int64_t ld_k, int64_t ld_v,
                               int32_t total_tokens, int32_t num_heads, int32_t head_dim, int32_t mode, void* q8,
@@ -278,7 +278,7 @@ fp8vit_status fp8vit_state_read(const void* d_state, fp8vit_state_view* out, voi
   std::memcpy(out->ring, h.ring, sizeof(out->ring));
   out->count = h.count;
   // The last dynamic forward's amax may still be pending: report the ring as
-  // it is once pushed (what the next amax pass does first on the device).
+  // it is once pushed (what the next dynamic forward's pass 2 does on the device).
   if (h.pending != 0u) {
     for (int x = 0; x < 3; ++x) out->ring[x][h.count % FP8VIT_RING_SLOTS] = h.pending_amax[x];
     out->count = h.count + 1;

@@ -111,8 +111,8 @@ __device__ __forceinline__ const uint4* chunk_src(const uint16_t* x, int64_t ld,
   return reinterpret_cast<const uint4*>(x + (int64_t)t * ld + 8 * (int64_t)j);
 }
 
-// NT: non-temporal loads and stores. They speed up the quantize pass of
-// dynamic mode (which re-reads what the amax pass has just read) by ~10 % and
+// NT: non-temporal loads and stores. They speed up a pass that re-reads what
+// the previous pass has just read (the redo of dynamic pass 2) by ~10 % and
 // slow the static pass slightly.
 template <bool NT>
 __device__ __forceinline__ uint4 ld16(const uint4* p) {

@@ -120,8 +120,8 @@ fp8vit_status fp8vit_load_static_scales(const char* json_path, const char* layer
  * Workflow, step 2 (serve with static scales: no dynamic overhead). */
 fp8vit_status fp8vit_state_set_static(void* d_state, const float values_qkv[3], void* stream);
 
-/* Dynamic scale bookkeeping alone (the same device code the fused quantizer
- * runs after its amax pass): push the three amax values at d_amax_qkv
+/* Dynamic scale bookkeeping alone (what the dynamic quantizer's second pass
+ * does, as a call of its own): push the three amax values at d_amax_qkv
  * (device, float[3], finite and >= 0) into the ring slot count % 16, advance
  * count, and set descale_used[i] = max(fp32(W_i / 448), 1e-10) where W_i is
  * the maximum over all 16 ring slots after the push (vLLM page, Usage: the
@@ -380,7 +380,7 @@ fp8vit_status fp8vit_state_read(const void* d_state, fp8vit_state_view* out, voi
 
 /* Synchronous write of a whole state, the inverse of fp8vit_state_read: ring,
  * count, static values, last descales, last amax, flags, cu_check and the
- * saturation counts are taken from `in`; the amax pass's partial maxima are
+ * saturation counts are taken from `in`; dynamic pass 1's partials are
  * cleared as by fp8vit_state_init, and no push is pending (a view from
  * fp8vit_state_read already has a pending push applied). With it a
  * calibration or a dynamic ring can be saved and resumed: the forwards that
