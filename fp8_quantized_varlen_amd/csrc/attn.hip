@@ -993,7 +993,9 @@ __device__ __forceinline__ void widen(const uint8_t* v8, uint8_t* vh, int wave, 
       lo[1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[0], 1.0f, true));
       hi[0] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[1], 1.0f, false));
       hi[1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[1], 1.0f, true));
-      if (c >= 72) {
+      // Only the units of column block 4 (the last n) reach column 72; the
+      // test on n is a constant once the loop is unrolled.
+      if (16 * ((WAVES * n + WAVES - 1) >> 2) + 15 >= 72 && c >= 72) {
         const int f = c == 72 ? 0x3c003c00 : 0;
         lo = v2i{f, f};
         hi = v2i{f, f};
