@@ -336,16 +336,17 @@ __global__ __launch_bounds__(kQuantThreads) void quant_fix_kernel(QuantArgs a) {
   const bool count_sat = (st->flags & FP8VIT_FLAG_COUNT_SATURATION) != 0u;
   // Everything the bookkeeping reads, loaded before the reduction so that the
   // loads overlap it (only block 0's first thread writes the state below).
-  float wo[3], pa[3];
+  float wo[3], pa[3] = {0.0f, 0.0f, 0.0f};
   uint32_t count = 0u, pend = 0u;
   if (threadIdx.x == 0) {
 #pragma unroll
-    for (int x = 0; x < 3; ++x) {
-      wo[x] = st->win_other[x];
-      pa[x] = st->pending_amax[x];
+    for (int x = 0; x < 3; ++x) wo[x] = st->win_other[x];
+    if (blockIdx.x == 0) {
+#pragma unroll
+      for (int x = 0; x < 3; ++x) pa[x] = st->pending_amax[x];
+      count = st->count;
+      pend = st->pending;
     }
-    count = st->count;
-    pend = st->pending;
   }
   uint32_t m[3] = {0u, 0u, 0u}, sat[3] = {0u, 0u, 0u};
   for (int b = threadIdx.x; b < a.amax_blocks; b += kQuantThreads) {
