@@ -532,10 +532,12 @@ def main():
         "scaling": "weak",
         "vs_baseline": round(value / PAGE_MI300X_TFLOPS[w.name], 3) if w.name in PAGE_MI300X_TFLOPS else None,
         # S = Q K^T on the FP8 MFMA; P.V on the f16 MFMA in the wide kernels,
-        # on the FP8 MFMA (two e4m3 terms of P) in the narrow ones
+        # on the FP8 MFMA (two e4m3 terms of P) in the narrow ones. The wide
+        # hd72 block-scaled kernel takes d 64..71 of S as exact scaled bf16.
         "dtype": ("fp8e4m3+f16" if kname.startswith("attn_w32") or
                   (kname.startswith("attn_kernel<128") and kname.split(", ")[2] == "true")
-                  else "fp8e4m3") + ("+e8m0 block scales (Q, K)" if mx else ""),
+                  else "fp8e4m3") + ("+e8m0 block scales (Q, K)" if mx else "")
+                 + ("+bf16 (S, d 64..71)" if mx and kname.startswith("attn_w32") else ""),
         "data": "synthetic",
         "config": {"workload": w.name, "segments": list(w.seglens), "heads": H, "head_dim": d, "output": args.out,
                    "key_split_workspace_bytes": ws_bytes if out8 is None and not mx else 0,

@@ -973,6 +973,22 @@ __device__ __forceinline__ v16f mfma16(long a, long b, const v16f& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a, b, c, 0, 0, 0);
 }
 
+// MX: d 64..71 (the 8 elements of block 2) as bf16 values code * 2^(e - 127),
+// exact (an e4m3 value times a power of two, inside bf16's range), for the
+// 32x32x16 bf16 product. e8 is the block's E8M0 byte; byte 0 (2^-127) gives
+// scale 0, which drops only values below 448 * 2^-127 in magnitude.
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ v8bf tail_bf16(long codes, uint32_t e8) {
+  const float sc = __uint_as_float(e8 << 23);
+  const int lo = (int)codes, hi = (int)(codes >> 32);
+  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, false);
+  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, true);
+  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, false);
+  const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, true);
+  return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 // One wave's share of widening the e4m3 V tile (80-byte rows) into the f16
 // operand layout above. Unit i = (16-column block cb, 8-key step sidx): lane
 // (g, i16) reads keys 32g + 8 sidx .. + 7 of column c = 16 cb + i16; keys
@@ -1255,9 +1271,10 @@ void attn_w32_kernel(AttnArgs a) {
       }
     }
   }
-  // MX: d 64..71 go through a second scaled 32x32x64 product (block 2 in
-  // positions 0..7 of lane half 0, everything else zero).
-  const v8i qb8 = v8i{(int)qbv, (int)(qbv >> 32), 0, 0, 0, 0, 0, 0};
+  // MX: d 64..71 (block 2) go through the 32x32x16 bf16 product as exact
+  // scaled values (lane half 0; half 1 and rows past the segment are zero).
+  v8bf qt;
+  if constexpr (MX) qt = tail_bf16(qbv, (uint32_t)qs2);
 
   v16f o[3];
 #pragma unroll
@@ -1285,17 +1302,13 @@ void attn_w32_kernel(AttnArgs a) {
   // dwords ksb; lane l's row is key 32u + l%32).
   auto s_block = [&](const lds_u8* kb, const uint32_t* ksb, int u) -> v16f {
     if constexpr (MX) {
-      // The second product's A operand is the first one's with dwords 0..1
-      // replaced by d 64..71: the other dwords (finite codes) meet zero Q
-      // dwords, and so does lane half 1 (its Q dwords 0..1 are zero too).
+      // d 0..63 on the scaled 32x32x64 product (blocks 0 and 1), d 64..71 as
+      // scaled bf16 values (lane half 1 holds the same key's bytes, which meet
+      // zero Q values).
       const uint32_t ksw = ((const __attribute__((address_space(3))) uint32_t*)ksb)[32 * u + l32];
-      const v8i ka = k_a(kb, u);
-      const long kbv = k_b(kb, u);
       const v16f s01 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          ka, qa, zero16, 0, 0, 0, (int)((ksw >> (8 * hf)) & 0xffu), 0, qs01);
-      const v8i kb8 = v8i{(int)kbv, (int)(kbv >> 32), ka[2], ka[3], ka[4], ka[5], ka[6], ka[7]};
-      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kb8, qb8, s01, 0, 0, 0, (int)((ksw >> 16) & 0xffu), 0,
-                                                             qs2);
+          k_a(kb, u), qa, zero16, 0, 0, 0, (int)((ksw >> (8 * hf)) & 0xffu), 0, qs01);
+      return __builtin_amdgcn_mfma_f32_32x32x16_bf16(tail_bf16(k_b(kb, u), (ksw >> 16) & 0xffu), qt, s01, 0, 0, 0);
     }
     return mfma16(k_b(kb, u), qbv, mfma64(k_a(kb, u), qa, zero16));
   };

@@ -333,8 +333,10 @@ fp8vit_status fp8vit_quantize_qkv_mx(const void* q, const void* k, const void* v
  * core (v_mfma_scale_f32_16x16x128_f8f6f4, which takes one E8M0 byte per
  * operand row and 32-element block); V uses the per-tensor descale in d_state.
  * Runs the kernel shapes fp8vit_attn_varlen chooses, with no key split
- * (head_dim 72 wide: v_mfma_scale_f32_32x32x64_f8f6f4 for d 0..63 and again
- * for d 64..71). bf16 output only. Arguments, layout and errors as
+ * (head_dim 72 wide: v_mfma_scale_f32_32x32x64_f8f6f4 for d 0..63; d 64..71
+ * as the exact bf16 values code * 2^(s_b) on the 32x32x16 bf16 product, where
+ * a block scale byte of 0 counts as scale 0 and so drops only values below
+ * 448 * 2^-127). bf16 output only. Arguments, layout and errors as
  * fp8vit_attn_varlen, with d_q_scales and d_k_scales
  * the [T, H, 4] scale bytes (device, 4-byte aligned, non-null unless the
  * problem is empty).
